@@ -1,0 +1,195 @@
+"""fp64 reference attention: materialised scores, two-pass softmax, P V, LSE.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+HIP path.  Every array is converted to float64 on entry; bf16 and fp32 inputs
+upcast exactly, so the oracle sees exactly the stored input values.
+
+Readings of the pages that this file fixes (page titles abbreviated):
+
+* Scale is a multiplier applied to Q K^T ("Attention三算子融合实战" 3.2 writes
+  the score as qk * scale with scale usually 1/sqrt(D); section 1.1's "divide
+  by the scaling factor" is the same thing with the reciprocal).
+* Causal: query i sees key j iff j <= i, diagonal included (same page, 4.3:
+  keys j > row get -inf).  Prefill has as many queries as keys.
+* GQA: query head h reads KV head g = h // (Hq / Hkv), i.e. contiguous groups
+  ("手写Triton kernel重构Qwen3.5-0.8B" 2.1 broadcasts 2 KV heads to 8 query
+  heads).
+* Layout [B, H, S, D], contiguous ("Attention三算子融合实战" 3.2 addresses a
+  row as head * S * D + row * D + d).
+* Decode cache is packed per sequence: sequence b is a [Hkv, L_b, D] block at
+  element offset Hkv * D * sum(L_0 .. L_{b-1}).  The single query of sequence b
+  attends to all L_b cached keys (it is the newest token; section 1.3 of the
+  same page: Q has one row while K and V grow with the history).
+* LSE is the natural-log log-sum-exp of the scaled, masked score row
+  ("triton-optimization" 3.5: m + log(d)).
+* A row with no visible key (L_b = 0) gives o = 0 and lse = -inf; the pages
+  never produce one.
+"""
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _kv_head(h, Hq, Hkv):
+    """KV head read by query head h: contiguous groups of Hq // Hkv heads."""
+    return h // (Hq // Hkv)
+
+
+def _check_heads(Hq, Hkv):
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
+
+
+def _visible(query_pos, n_keys, causal):
+    """Boolean [len(query_pos), n_keys]: may query at position i see key j?"""
+    j = np.arange(n_keys)[None, :]
+    if causal:
+        return j <= np.asarray(query_pos)[:, None]
+    return np.ones((len(query_pos), n_keys), dtype=bool)
+
+
+def _two_pass_softmax(s, visible):
+    """Row softmax of the scores s over the visible entries, in two passes.
+
+    Pass 1 takes the row max m over visible scores; pass 2 exponentiates
+    s - m, sums to l and divides.  Returns (P, lse) with lse = m + ln(l).
+    Invisible entries get probability 0 (a -inf score).  Rows with no visible
+    entry return P = 0 and lse = -inf.
+    """
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=-1, initial=-np.inf)                  # pass 1
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    p = np.where(visible, np.exp(s - m_safe[..., None]), 0.0)   # pass 2
+    l = p.sum(axis=-1)
+    l_safe = np.where(empty, 1.0, l)
+    P = p / l_safe[..., None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return P, lse
+
+
+def softmax_probabilities(q, k, scale, causal):
+    """The probability matrix P [B, Hq, S, S] of prefill attention."""
+    q, k = _f64(q), _f64(k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _check_heads(Hq, Hkv)
+    P = np.zeros((B, Hq, S, S))
+    vis = _visible(np.arange(S), S, causal)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = scale * (q[b, h] @ k[b, g].T)
+            P[b, h], _ = _two_pass_softmax(s, vis)
+    return P
+
+
+def prefill(q, k, v, scale, causal):
+    """Prefill attention.  q [B,Hq,S,D]; k, v [B,Hkv,S,D].
+
+    Returns (o [B,Hq,S,D], lse [B,Hq,S]) in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _check_heads(Hq, Hkv)
+    if k.shape != (B, Hkv, S, D) or v.shape != (B, Hkv, S, D):
+        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    o = np.zeros((B, Hq, S, D))
+    lse = np.zeros((B, Hq, S))
+    vis = _visible(np.arange(S), S, causal)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = scale * (q[b, h] @ k[b, g].T)            # materialised S
+            P, lse[b, h] = _two_pass_softmax(s, vis)
+            o[b, h] = P @ v[b, g]
+    return o, lse
+
+
+def prefill_rows(q, k, v, scale, causal, rows):
+    """Prefill attention evaluated only at selected query rows.
+
+    rows: int array [Hq, R]; head h is evaluated at rows[h] (the same rows for
+    every batch entry).  Returns (o [B,Hq,R,D], lse [B,Hq,R]).  Each selected
+    row is the same computation as in ``prefill``; only the score rows that
+    are needed are materialised.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _check_heads(Hq, Hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    R = rows.shape[1]
+    o = np.zeros((B, Hq, R, D))
+    lse = np.zeros((B, Hq, R))
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            r = rows[h]
+            s = scale * (q[b, h, r] @ k[b, g].T)
+            P, lse[b, h] = _two_pass_softmax(s, _visible(r, S, causal))
+            o[b, h] = P @ v[b, g]
+    return o, lse
+
+
+def decode(q, kcache, vcache, seqlens, scale, Hkv):
+    """Decode attention: one query row per sequence against its whole cache.
+
+    q [B,Hq,D]; kcache, vcache: flat packed caches (sequence b is a
+    [Hkv, L_b, D] block at element offset Hkv*D*sum(L[:b])); seqlens [B].
+    Returns (o [B,Hq,D], lse [B,Hq]).
+    """
+    q = _f64(q)
+    kc, vc = _f64(kcache).reshape(-1), _f64(vcache).reshape(-1)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    B, Hq, D = q.shape
+    _check_heads(Hq, Hkv)
+    if kc.size != Hkv * D * int(seqlens.sum()) or vc.size != kc.size:
+        raise ValueError("packed caches do not match seqlens")
+    o = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    off = 0
+    for b in range(B):
+        L = int(seqlens[b])
+        kb = kc[off: off + Hkv * L * D].reshape(Hkv, L, D)
+        vb = vc[off: off + Hkv * L * D].reshape(Hkv, L, D)
+        off += Hkv * L * D
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = scale * (kb[g] @ q[b, h])                 # [L]
+            P, row_lse = _two_pass_softmax(s[None, :],
+                                           np.ones((1, L), dtype=bool))
+            lse[b, h] = row_lse[0]
+            o[b, h] = (P @ vb[g])[0]
+    return o, lse
+
+
+def lse_combine(o_parts, lse_parts):
+    """Merge attention results computed over disjoint key chunks.
+
+    o_parts [n, ..., D]: each chunk's normalised output; lse_parts [n, ...]:
+    each chunk's LSE (-inf for an empty chunk).  With M = max_s lse_s and
+    w_s = exp(lse_s - M): o = sum_s w_s o_s / sum_s w_s and
+    lse = M + ln(sum_s w_s).  This is the cross-chunk merge of the online
+    softmax state ("Attention三算子融合实战" 2.2: the merge order does not
+    matter as long as m and l are kept; 4.4: key chunks processed by separate
+    blocks are merged afterwards).  All chunks empty gives o = 0, lse = -inf.
+    """
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    M = lse_parts.max(axis=0)
+    empty = ~np.isfinite(M)
+    M_safe = np.where(empty, 0.0, M)
+    w = np.exp(lse_parts - M_safe[None])
+    w = np.where(np.isfinite(lse_parts), w, 0.0)
+    W = w.sum(axis=0)
+    W_safe = np.where(empty, 1.0, W)
+    o = (w[..., None] * o_parts).sum(axis=0) / W_safe[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, M_safe + np.log(W_safe))
+    return o, lse
