@@ -1,0 +1,178 @@
+"""Python binding of libattn.so: argument marshalling only.
+
+Each function checks tensor devices, dtypes, shapes and contiguity, allocates
+outputs with torch, and calls the C entry point of the same name on torch's
+current HIP stream.  Every step of the computation runs in the library's
+kernels; there is no host fallback, and a missing library is an error.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "libattn.so")
+_lib = None
+
+STATUS = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE",
+    -3: "ATTN_ERR_GQA", -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_ALIGN",
+    -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_SPLITS", -8: "ATTN_ERR_LAUNCH",
+    -9: "ATTN_ERR_SCALE",
+}
+MAX_SPLITS = 256
+
+
+class AttnError(ValueError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__(f"{fn} returned {status} "
+                         f"({status_string(status)})")
+
+
+def lib():
+    """The loaded library (built by ``causal_attention_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m causal_attention_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, \
+            ctypes.c_size_t
+        L.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_prefill.restype = i
+        L.attn_prefill_f32.argtypes = L.attn_prefill.argtypes
+        L.attn_prefill_f32.restype = i
+        L.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
+        L.attn_decode_workspace_size.restype = sz
+        L.attn_decode_auto_splits.argtypes = [i, i]
+        L.attn_decode_auto_splits.restype = i
+        L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
+                                  vp, sz, vp]
+        L.attn_decode.restype = i
+        L.attn_status_string.argtypes = [i]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
+                 with_lse=True):
+    """Fused prefill attention.
+
+    q [B,Hq,S,D]; k, v [B,Hkv,S,D]; bf16 (calls ``attn_prefill``) or fp32
+    (calls ``attn_prefill_f32``).  Returns (o, lse) with o like q and lse
+    fp32 [B,Hq,S] (None when ``with_lse`` is False).  ``scale`` defaults to
+    1/sqrt(D).
+    """
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    _check(q, "q", dtype, 4)
+    _check(k, "k", dtype, 4)
+    _check(v, "v", dtype, 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if lse.shape != (B, Hq, S):
+            raise ValueError("lse must be [B,Hq,S]")
+    fn = lib().attn_prefill if dtype == torch.bfloat16 else \
+        lib().attn_prefill_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
+            D, float(scale), int(bool(causal)), _stream())
+    if st != 0:
+        raise AttnError(st, fn.__name__)
+    return out, lse
+
+
+def attn_decode_auto_splits(B, Hkv):
+    return int(lib().attn_decode_auto_splits(int(B), int(Hkv)))
+
+
+def attn_decode_workspace_size(B, Hq, Hkv, D, num_splits=0):
+    n = int(lib().attn_decode_workspace_size(B, Hq, Hkv, D, num_splits))
+    if n == 0 and B > 0:
+        raise ValueError("invalid decode sizes")
+    return n
+
+
+def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
+                out=None, with_lse=False, lse=None, workspace=None):
+    """Split-K decode attention over a packed per-sequence KV cache.
+
+    q [B,Hq,D] bf16; kcache, vcache flat bf16 caches where sequence b is a
+    [Hkv, L_b, D] block; seqlens int32 [B] on the GPU.  Returns (o, lse);
+    lse is fp32 [B,Hq] or None.  ``workspace`` (uint8 GPU tensor) is
+    allocated when not given.
+    """
+    _check(q, "q", torch.bfloat16, 3)
+    _check(kcache, "kcache", torch.bfloat16, None)
+    _check(vcache, "vcache", torch.bfloat16, None)
+    _check(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, D = q.shape
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if kcache.numel() != vcache.numel():
+        raise ValueError("kcache and vcache must have the same size")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+    need = attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) if B else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    _check(workspace, "workspace", torch.uint8, 1)
+    st = lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens),
+                           _ptr(out), B, Hq, Hkv, D, float(scale),
+                           int(num_splits), _ptr(lse), _ptr(workspace),
+                           workspace.numel(), _stream())
+    if st != 0:
+        raise AttnError(st, "attn_decode")
+    return out, lse

@@ -1,0 +1,248 @@
+// C-ABI entry points of libattn.so: host-side validation, tile choice and
+// kernel launches.  Declarations and the contract live in include/attn.h.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "decode.hpp"
+#include "prefill.hpp"
+
+namespace {
+
+using attn::kDecodeThreads;
+using attn::kPrefillBM;
+using attn::kPrefillThreads;
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Common shape checks of both prefill entry points.
+int check_prefill(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, int B, int Hq, int Hkv, int S, int D,
+                  float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (Hq == 0 || Hkv == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  // Grid size: one workgroup per (batch, query head, 128-row tile).
+  const long long tiles = ((long long)S + kPrefillBM - 1) / kPrefillBM;
+  if ((long long)B * Hq * tiles > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if (B == 0 || S == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+template <typename T, template <int, bool> class Launcher>
+int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
+                   int B, int Hq, int Hkv, int S, int D, float scale,
+                   int causal, void* stream) {
+  const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
+  const dim3 grid((unsigned)(B * Hq * n_qtiles));
+  const dim3 block(kPrefillThreads);
+  const float sl2 = scale * attn::kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (D == 64) {
+    if (causal)
+      Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
+                              sl2, n_qtiles);
+    else
+      Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
+                               S, sl2, n_qtiles);
+  } else {
+    if (causal)
+      Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
+                               S, sl2, n_qtiles);
+    else
+      Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
+                                S, sl2, n_qtiles);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <int D, bool C>
+struct Bf16Prefill {
+  static void run(dim3 g, dim3 b, hipStream_t st, const __bf16* q,
+                  const __bf16* k, const __bf16* v, __bf16* o, float* lse,
+                  int B, int Hq, int Hkv, int S, float sl2, int nq) {
+    hipLaunchKernelGGL((attn::attn_prefill_bf16_kernel<D, C>), g, b, 0, st, q,
+                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq);
+  }
+};
+
+template <int D, bool C>
+struct F32Prefill {
+  static void run(dim3 g, dim3 b, hipStream_t st, const float* q,
+                  const float* k, const float* v, float* o, float* lse, int B,
+                  int Hq, int Hkv, int S, float sl2, int nq) {
+    hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
+                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq);
+  }
+};
+
+// ------------------------------------------------------------------ decode
+
+int auto_splits(int B, int Hkv) {
+  // Aim for about 4096 split workgroups (16 per CU over 256 CUs) so the
+  // whole cache streams in roughly one wave of resident workgroups.
+  const long long pairs = (long long)B * Hkv;
+  if (pairs <= 0) return 1;
+  long long ns = (4096 + pairs - 1) / pairs;
+  if (ns < 1) ns = 1;
+  if (ns > 128) ns = 128;
+  return (int)ns;
+}
+
+int check_decode_sizes(int B, int Hq, int Hkv, int D, int num_splits) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || D < 0) return ATTN_ERR_SHAPE;
+  if (Hq == 0 || Hkv == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_ERR_GQA;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  if ((long long)B * Hkv > 65535LL * 65535LL || B > 65535 || Hkv > 65535)
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+size_t workspace_bytes_for(int B, int Hq, int D, int ns) {
+  // fp32 partial outputs [B, Hq, ns, D] followed by partial LSEs [B, Hq, ns],
+  // the LSE block starting on a 16-byte boundary.
+  const size_t rows = (size_t)B * Hq * ns;
+  size_t o_bytes = rows * D * sizeof(float);
+  o_bytes = (o_bytes + 15) / 16 * 16;
+  return o_bytes + rows * sizeof(float);
+}
+
+template <int D, int G>
+void launch_decode_dg(const __bf16* q, const __bf16* kc, const __bf16* vc,
+                      const int* seqlens, __bf16* o, float* lse, float* ws_o,
+                      float* ws_lse, int B, int Hkv, int ns, float sl2,
+                      hipStream_t st) {
+  const dim3 grid(ns, Hkv, B);
+  hipLaunchKernelGGL((attn::attn_decode_split_kernel<D, G>), grid,
+                     dim3(kDecodeThreads), 0, st, q, kc, vc, seqlens, ws_o,
+                     ws_lse, Hkv, ns, sl2);
+  hipLaunchKernelGGL((attn::attn_decode_combine_kernel<D>),
+                     dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, seqlens,
+                     o, lse, Hkv * G, ns);
+}
+
+template <int D>
+void launch_decode_d(int G, const __bf16* q, const __bf16* kc,
+                     const __bf16* vc, const int* seqlens, __bf16* o,
+                     float* lse, float* ws_o, float* ws_lse, int B, int Hkv,
+                     int ns, float sl2, hipStream_t st) {
+  switch (G) {
+    case 1: launch_decode_dg<D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                   B, Hkv, ns, sl2, st); break;
+    case 2: launch_decode_dg<D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                   B, Hkv, ns, sl2, st); break;
+    case 4: launch_decode_dg<D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                   B, Hkv, ns, sl2, st); break;
+    default: launch_decode_dg<D, 8>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                    B, Hkv, ns, sl2, st); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 float* lse, int B, int Hq, int Hkv, int S, int D,
+                 float scale, int causal, void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK || empty) return st;
+  return launch_prefill<__bf16, Bf16Prefill>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
+      S, D, scale, causal, stream);
+}
+
+int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
+                     float* lse, int B, int Hq, int Hkv, int S, int D,
+                     float scale, int causal, void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK || empty) return st;
+  return launch_prefill<float, F32Prefill>(q, k, v, o, lse, B, Hq, Hkv, S, D,
+                                           scale, causal, stream);
+}
+
+int attn_decode_auto_splits(int B, int Hkv) { return auto_splits(B, Hkv); }
+
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
+                                  int num_splits) {
+  if (check_decode_sizes(B, Hq, Hkv, D, num_splits) != ATTN_OK) return 0;
+  const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  return workspace_bytes_for(B, Hq, D, ns);
+}
+
+int attn_decode(const void* q, const void* kcache, const void* vcache,
+                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                float scale, int num_splits, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0) return ATTN_OK;
+  if (!q || !kcache || !vcache || !seqlens || !o || !workspace)
+    return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) ||
+      !aligned(o, 2) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
+      !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  if (workspace_bytes < workspace_bytes_for(B, Hq, D, ns))
+    return ATTN_ERR_WORKSPACE;
+
+  const size_t rows = (size_t)B * Hq * ns;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = reinterpret_cast<float*>(
+      static_cast<char*>(workspace) + (rows * D * sizeof(float) + 15) / 16 * 16);
+  const int G = Hq / Hkv;
+  const float sl2 = scale * attn::kLog2e;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(kcache);
+  const __bf16* vb = static_cast<const __bf16*>(vcache);
+  __bf16* ob = static_cast<__bf16*>(o);
+  if (D == 64)
+    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B, Hkv,
+                        ns, sl2, hs);
+  else
+    launch_decode_d<128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B,
+                         Hkv, ns, sl2, hs);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+    case ATTN_ERR_GQA: return "ATTN_ERR_GQA";
+    case ATTN_ERR_HEAD_DIM: return "ATTN_ERR_HEAD_DIM";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_SPLITS: return "ATTN_ERR_SPLITS";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+    case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

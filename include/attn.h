@@ -1,0 +1,133 @@
+/*
+ * attn.h -- fused scaled-dot-product attention on MI355X (gfx950), C ABI.
+ *
+ * The operation is the attention chain of "Attention三算子融合实战：从Triton到
+ * CUDA的推理加速优化" (section 1.1): scores S = Q K^T times a scale, a row-wise
+ * softmax P of S, and O = P V, computed in one kernel with the online softmax
+ * of section 2.2 (running row max m and sum l, old terms rescaled by
+ * exp(m - m_new)) so that S and P never reach device memory (section 2.3).
+ * The causal mask is that of section 4.3: query row i sees key j only when
+ * j <= i.  Grouped-query attention follows "手写Triton kernel重构Qwen3.5-0.8B"
+ * (section 2.1: two KV heads serve eight query heads): query head h reads KV
+ * head h / (Hq / Hkv).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    row-major, 16-byte aligned (lse: 4-byte aligned).  The library never
+ *    allocates, frees or synchronises; it only enqueues kernels on `stream`
+ *    (a hipStream_t; NULL means the default stream) and returns.
+ *  - Every argument check runs on the host before any HIP call; a failed
+ *    check returns a negative attn_status and enqueues nothing.  Errors are
+ *    never printed or raised.  ATTN_ERR_LAUNCH reports a failed kernel launch.
+ *  - Empty work (B == 0, or S == 0 for prefill) returns ATTN_OK and enqueues
+ *    nothing.
+ *  - Outputs must not alias inputs.  The library holds no state between
+ *    calls: calls on different streams are independent, and a call may be
+ *    captured into a HIP graph.
+ *  - Accumulation is fp32 throughout (running m, l and the output
+ *    accumulator); bf16 results are rounded to nearest even.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,     /* a negative size, or a size too large to index */
+  ATTN_ERR_GQA = -3,       /* Hq or Hkv <= 0, Hq % Hkv != 0, or an
+                              unsupported group size Hq / Hkv */
+  ATTN_ERR_HEAD_DIM = -4,  /* D is not 64 or 128 */
+  ATTN_ERR_ALIGN = -5,     /* a pointer is not aligned as required */
+  ATTN_ERR_WORKSPACE = -6, /* decode workspace smaller than required */
+  ATTN_ERR_SPLITS = -7,    /* num_splits < 0 or > ATTN_MAX_SPLITS */
+  ATTN_ERR_LAUNCH = -8,    /* the HIP runtime rejected a kernel launch */
+  ATTN_ERR_SCALE = -9      /* scale is not a finite number */
+} attn_status;
+
+/* Largest num_splits attn_decode accepts. */
+#define ATTN_MAX_SPLITS 256
+
+/*
+ * Prefill attention, bf16 storage.
+ *   q, o : [B, Hq,  S, D] bf16     k, v : [B, Hkv, S, D] bf16
+ *   lse  : [B, Hq,  S]    fp32     natural-log log-sum-exp of each scaled,
+ *                                   masked score row (m + ln l; the form of
+ *                                   the "triton-optimization" page, section
+ *                                   3.5); may be NULL to skip it.
+ *   scale: multiplier of Q K^T (1/sqrt(D) in the usual setting; the fused
+ *          Triton kernel of the attention-fusion page, section 3.2, applies it
+ *          to qk before the softmax).
+ *   causal: nonzero for the causal mask j <= i, zero for no mask.
+ * Any S >= 0 is accepted (tail tiles are masked, as section 6.1 of the
+ * attention-fusion page requires).  D must be 64 or 128.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 float* lse, int B, int Hq, int Hkv, int S, int D,
+                 float scale, int causal, void* stream);
+
+/*
+ * Prefill attention, fp32 storage.  Same arguments and layouts as
+ * attn_prefill with every tensor fp32.  The probabilities P stay fp32 (the
+ * accuracy setting of the attention-fusion page, sections 3.3 and 5.5).
+ */
+int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
+                     float* lse, int B, int Hq, int Hkv, int S, int D,
+                     float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode needs for these sizes
+ * (num_splits == 0 selects the same automatic split count attn_decode uses).
+ * Returns 0 when the sizes are invalid.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
+                                  int num_splits);
+
+/* The split count attn_decode uses for num_splits == 0 (depends on B and
+   Hkv only: nothing is read back from the device). */
+int attn_decode_auto_splits(int B, int Hkv);
+
+/*
+ * Decode attention: one query row per sequence against its whole KV cache
+ * (the decode setting of the attention-fusion page, section 1.3: Q has one
+ * row while K and V grow with the history), split over the cache length and
+ * merged with a log-sum-exp combine (section 4.4: key chunks handled by
+ * separate blocks and merged afterwards; section 2.2: the merge order does
+ * not matter once m and l are kept).
+ *   q, o     : [B, Hq, D] bf16
+ *   kcache,
+ *   vcache   : packed per sequence: sequence b is a [Hkv, L_b, D] bf16 block
+ *              at element offset Hkv * D * (L_0 + ... + L_{b-1}).
+ *   seqlens  : DEVICE int32 [B], L_b = number of cached keys the query of
+ *              sequence b attends to (its own key included).  L_b <= 0 gives
+ *              o = 0 and lse = -inf for that sequence.
+ *   num_splits: key chunks per sequence, 1..ATTN_MAX_SPLITS, or 0 for
+ *              attn_decode_auto_splits(B, Hkv).  A sequence is cut into at
+ *              most num_splits chunks of at least 64 keys.
+ *   lse      : [B, Hq] fp32 natural-log LSE, or NULL.
+ *   workspace: DEVICE scratch of at least
+ *              attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) bytes,
+ *              16-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and are overwritten.  Two calls in flight at
+ *              once must not share a workspace.
+ * Supported group sizes Hq / Hkv: 1, 2, 4, 8.
+ */
+int attn_decode(const void* q, const void* kcache, const void* vcache,
+                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                float scale, int num_splits, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* A static description of a status code ("ATTN_OK", ...). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+bad arguments on the host before any HIP call (so no GPU is needed here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_attention_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x10000    # fake, 16-byte aligned "device" address: never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["attn_prefill", "attn_prefill_f32", "attn_decode",
+              "attn_decode_workspace_size", "attn_decode_auto_splits",
+              "attn_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = attn.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in attn.STATUS.items():
+        assert attn.status_string(code) == name
+    assert attn.status_string(-99) == "ATTN_ERR_UNKNOWN"
+
+
+def prefill(fn="attn_prefill", q=A, k=A, v=A, o=A, lse=A, B=1, Hq=8, Hkv=2,
+            S=64, D=128, scale=0.1, causal=1):
+    L = attn.lib()
+    return getattr(L, fn)(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal,
+                          None)
+
+
+@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f32"])
+def test_prefill_argument_errors(fn):
+    assert prefill(fn, B=-1) == -2
+    assert prefill(fn, S=-5) == -2
+    assert prefill(fn, Hq=8, Hkv=3) == -3
+    assert prefill(fn, Hq=0) == -3
+    assert prefill(fn, Hkv=0) == -3
+    assert prefill(fn, D=96) == -4
+    assert prefill(fn, D=256) == -4
+    assert prefill(fn, q=None) == -1
+    assert prefill(fn, v=None) == -1
+    assert prefill(fn, o=A + 8) == -5
+    assert prefill(fn, lse=A + 2) == -5
+    assert prefill(fn, scale=float("nan")) == -9
+    assert prefill(fn, scale=float("inf")) == -9
+    # grid too large for one launch
+    assert prefill(fn, B=65536, Hq=1024, Hkv=1, S=1 << 20) == -2
+
+
+@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f32"])
+def test_prefill_empty_is_a_noop(fn):
+    # B == 0 or S == 0: nothing to do, even with NULL pointers
+    assert prefill(fn, q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+    assert prefill(fn, q=None, k=None, v=None, o=None, lse=None, S=0) == 0
+
+
+def decode(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, scale=0.1,
+           ns=0, lse=None, ws=A, wsb=1 << 30):
+    L = attn.lib()
+    return L.attn_decode(q, kc, vc, sl, o, B, Hq, Hkv, D, scale, ns, lse, ws,
+                         wsb, None)
+
+
+def test_decode_argument_errors():
+    assert decode(B=-1) == -2
+    assert decode(Hq=8, Hkv=3) == -3
+    assert decode(Hq=12, Hkv=1) == -3      # group size 12 not compiled
+    assert decode(D=80) == -4
+    assert decode(ns=-1) == -7
+    assert decode(ns=attn.MAX_SPLITS + 1) == -7
+    assert decode(q=None) == -1
+    assert decode(sl=None) == -1
+    assert decode(ws=None) == -1
+    assert decode(sl=A + 2) == -5
+    assert decode(ws=A + 4) == -5
+    assert decode(wsb=100) == -6
+    assert decode(scale=float("nan")) == -9
+    assert decode(B=0, q=None, kc=None, vc=None, sl=None, o=None, ws=None) == 0
+
+
+def test_decode_workspace_size():
+    L = attn.lib()
+    ns = attn.attn_decode_auto_splits(32, 2)
+    assert 1 <= ns <= attn.MAX_SPLITS
+    rows = 32 * 8 * ns
+    want = (rows * 128 * 4 + 15) // 16 * 16 + rows * 4
+    assert L.attn_decode_workspace_size(32, 8, 2, 128, 0) == want
+    assert L.attn_decode_workspace_size(32, 8, 2, 128, 5) == \
+        32 * 8 * 5 * 128 * 4 + 32 * 8 * 5 * 4
+    assert L.attn_decode_workspace_size(32, 8, 3, 128, 5) == 0
+    assert L.attn_decode_workspace_size(32, 8, 2, 128, -1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_prefill(x, x, x)

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances: max abs error on O of 1e-5 for fp32 storage and 2e-2 for bf16
+storage (fp32 accumulation inside the kernels), and 1e-3 on the natural-log
+LSE.  Inputs are seeded synthetic tensors; the oracle sees exactly the stored
+(bf16-rounded) values.
+
+The 1e-5 / 2e-2 bounds are for unit-variance inputs.  For the input-scale
+sweep (sigma != 1) the bound is derived from the arithmetic, see ``o_tol``:
+with bf16 storage the error is the relative rounding of P and O (2^-9), so it
+scales with the value magnitude sigma; with fp32 storage it is the fp32
+accumulation error of the scores, which grows with |q||k| ~ sigma^2 sqrt(D)
+and moves O in proportion to |v| ~ sigma, so it scales with sigma^3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_attention_amd import attn, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LSE_TOL = 1e-3
+
+
+def o_tol(dtype, sigma=1.0):
+    s = max(1.0, sigma)
+    return 1e-5 * s ** 3 if dtype == "f32" else 2e-2 * s
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_prefill(B, Hq, Hkv, S, D, dtype, causal, sigma=1.0, seed=0,
+                scale=None):
+    say(f"[prefill] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} {dtype} "
+        f"causal={causal} sigma={sigma} seed={seed}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, dtype, sigma, seed)
+    scale = 1 / math.sqrt(D) if scale is None else scale
+    o, lse = attn.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV),
+                               causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse, scale
+
+
+def check_prefill(B, Hq, Hkv, S, D, dtype, causal, sigma=1.0, seed=0):
+    q, k, v, o, lse, scale = run_prefill(B, Hq, Hkv, S, D, dtype, causal,
+                                         sigma, seed)
+    ro, rl = oracle.prefill(np64(q), np64(k), np64(v), scale, causal)
+    eo = np.abs(np64(o) - ro)
+    el = np.abs(lse.cpu().numpy() - rl)
+    worst = np.unravel_index(np.argmax(eo), eo.shape) if eo.size else None
+    say(f"   max|dO|={eo.max() if eo.size else 0:.3e} "
+        f"mean|dO|={eo.mean() if eo.size else 0:.3e} at {worst} "
+        f"max|dLSE|={el.max() if el.size else 0:.3e}")
+    assert np.isfinite(np64(o)).all()
+    if eo.size:
+        assert eo.max() <= o_tol(dtype, sigma)
+        assert el.max() <= LSE_TOL
+
+
+# ------------------------------------------------------------ the workloads
+
+def test_c1_single_head_fp32():
+    w = inputs.WORKLOADS["c1_f32_s128"]
+    check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
+
+
+def test_c2_mha12_s512():
+    w = inputs.WORKLOADS["c2_mha12_s512"]
+    check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
+
+
+def test_c3_gqa_b4_s2048():
+    w = inputs.WORKLOADS["c3_gqa_b4_s2048"]
+    check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
+
+
+def test_c5_long_context_sampled_rows():
+    w = inputs.WORKLOADS["c5_gqa_s32768"]
+    q, k, v, o, lse, scale = run_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype,
+                                         w.causal, w.sigma)
+    rows = inputs.sampled_rows(w.Hq, w.S, w.sampled_rows)
+    ro, rl = oracle.prefill_rows(np64(q), np64(k), np64(v), scale, True, rows)
+    o_c, l_c = o.cpu(), lse.cpu()
+    go = np.stack([np64(o_c[:, h, rows[h]]) for h in range(w.Hq)], axis=1)
+    gl = np.stack([l_c[:, h, rows[h]].numpy() for h in range(w.Hq)], axis=1)
+    eo, el = np.abs(go - ro).max(), np.abs(gl - rl).max()
+    say(f"   sampled rows: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= 2e-2 and el <= LSE_TOL
+    # every row, checked by properties that hold at any size: finite, and
+    # |o| bounded by the largest |v| of its KV head (o is a convex
+    # combination of value rows)
+    vmax = v.float().abs().amax(dim=(2, 3))           # [B, Hkv]
+    omax = o.float().abs().amax(dim=(2, 3)).cpu()     # [B, Hq]
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    G = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        assert omax[0, h] <= vmax[0, h // G] * (1 + 2 ** -8)
+
+
+# ------------------------------------------------------- edge shapes, masks
+
+@pytest.mark.parametrize("S", [1, 2, 7, 63, 64, 65, 127, 129, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (12, 12), (8, 2), (8, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_edge_shapes_bf16(S, D, Hq, Hkv, causal):
+    check_prefill(2 if S < 200 else 1, Hq, Hkv, S, D, "bf16", causal,
+                  seed=S + D)
+
+
+@pytest.mark.parametrize("S", [1, 33, 128, 129, 300])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_edge_shapes_f32(S, D, causal):
+    check_prefill(1, 4, 2, S, D, "f32", causal, seed=S)
+
+
+@pytest.mark.parametrize("sigma", [0.01, 1.0, 4.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_value_scale_sweep(sigma, dtype):
+    check_prefill(1, 8, 2, 257, 128, dtype, True, sigma=sigma, seed=7)
+
+
+def test_prefill_is_deterministic():
+    w = inputs.WORKLOADS["c3_gqa_b4_s2048"]
+    q, k, v = (t.to(DEV) for t in
+               inputs.prefill_inputs(1, 8, 2, 1031, 128, "bf16", 1.0, 3))
+    o1, l1 = attn.attn_prefill(q, k, v)
+    o2, l2 = attn.attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_without_lse():
+    q, k, v = (t.to(DEV) for t in
+               inputs.prefill_inputs(1, 8, 2, 100, 128, "bf16", 1.0, 4))
+    o1, _ = attn.attn_prefill(q, k, v)
+    o2, l2 = attn.attn_prefill(q, k, v, with_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+# -------------------------------------------------------------------- decode
+
+def run_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
+    say(f"[decode] B={len(seqlens)} Hq={Hq} Hkv={Hkv} D={D} "
+        f"ns={num_splits} sum(L)={int(np.sum(seqlens))} seed={seed}")
+    sl, q, kc, vc = inputs.decode_inputs(len(seqlens), Hq, Hkv, D,
+                                         seqlens=seqlens, sigma=sigma,
+                                         seed=seed)
+    o, lse = attn.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV),
+                              torch.from_numpy(sl).to(DEV), Hkv=Hkv,
+                              num_splits=num_splits, with_lse=True)
+    torch.cuda.synchronize()
+    return sl, q, kc, vc, o, lse
+
+
+def check_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
+    sl, q, kc, vc, o, lse = run_decode(seqlens, Hq, Hkv, D, num_splits,
+                                       sigma, seed)
+    ro, rl = oracle.decode(np64(q), np64(kc), np64(vc), sl, 1 / math.sqrt(D),
+                           Hkv)
+    go, gl = np64(o), lse.cpu().numpy()
+    empty = np.asarray(sl) <= 0
+    assert (go[empty] == 0).all() and np.isneginf(gl[empty]).all()
+    live = ~empty
+    if live.any():
+        eo = np.abs(go[live] - ro[live]).max()
+        el = np.abs(gl[live] - rl[live]).max()
+        say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= o_tol("bf16", sigma) and el <= LSE_TOL
+    return o, lse
+
+
+def test_c4_decode_b32():
+    w = inputs.WORKLOADS["c4_decode_b32"]
+    sl = inputs.decode_seqlens(w.B, w.lmin, w.lmax, w.seed)
+    check_decode(sl, w.Hq, w.Hkv, w.D, num_splits=0, sigma=w.sigma,
+                 seed=w.seed)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 16, 0])
+def test_decode_lengths_and_splits(num_splits):
+    check_decode([1, 15, 16, 17, 255, 4096, 64, 65, 129], 8, 2, 128,
+                 num_splits=num_splits, seed=11)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (8, 8), (8, 2), (8, 1), (4, 2)])
+def test_decode_heads_and_dims(D, Hq, Hkv):
+    check_decode([5, 700, 2000], Hq, Hkv, D, seed=D + Hq)
+
+
+def test_decode_empty_sequences():
+    check_decode([0, 10, 0, 300], 8, 2, 128, seed=5)
+
+
+@pytest.mark.parametrize("sigma", [0.01, 4.0])
+def test_decode_value_scale(sigma):
+    check_decode([100, 1500], 8, 2, 128, sigma=sigma, seed=9)
+
+
+def test_decode_split_count_changes_only_rounding():
+    ref = None
+    for ns in [1, 4, 64, 256]:
+        o, lse = run_decode([3000, 200], 8, 2, 128, num_splits=ns, seed=2)[4:]
+        if ref is None:
+            ref = (o.float(), lse)
+        else:
+            assert (o.float() - ref[0]).abs().max() <= 2e-2
+            assert (lse - ref[1]).abs().max() <= 1e-4
+
+
+def test_decode_equals_last_prefill_row():
+    Hq, Hkv, D, L = 8, 2, 128, 333
+    q, k, v = inputs.prefill_inputs(1, Hq, Hkv, L, D, "bf16", 1.0, 21)
+    po, pl = attn.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    qd = q[:, :, L - 1].contiguous()
+    kc, vc = k[0].reshape(-1), v[0].reshape(-1)
+    o, lse = attn.attn_decode(qd.to(DEV), kc.to(DEV), vc.to(DEV),
+                              torch.tensor([L], dtype=torch.int32,
+                                           device=DEV),
+                              Hkv=Hkv, with_lse=True)
+    torch.cuda.synchronize()
+    assert (o.float() - po[:, :, L - 1].float()).abs().max() <= 2e-2
+    assert (lse - pl[:, :, L - 1]).abs().max() <= 1e-4
+
+
+def test_decode_is_deterministic():
+    sl, q, kc, vc = inputs.decode_inputs(8, 8, 2, 128, lmin=1, lmax=3000,
+                                         seed=4)
+    args = (q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(sl).to(DEV))
+    o1, l1 = attn.attn_decode(*args, Hkv=2, with_lse=True)
+    o2, l2 = attn.attn_decode(*args, Hkv=2, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
