@@ -1,0 +1,219 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = one causal GQA prefill (batch 4, 8 query heads over 2 KV heads,
+head_dim 128, seq 2048, bf16) followed by one split-K decode (batch 32, same
+heads, per-sequence cache length uniform in [256, 4096] from seed 0, bf16),
+each through the C ABI on torch's current stream.  Inputs are seeded
+synthetic tensors resident in HBM before timing; several input copies are
+rotated so consecutive steps do not find their inputs in the 256 MB
+last-level cache.
+
+Prints ONE JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
+(4*D per visible query/key pair, causal pairs only) over the prefill kernel's
+average duration measured with HIP events; the decode's KV-cache GB/s
+(K and V bytes read once per KV head, plus q and o) is in ``decode``.  Both
+carry a ``roofline`` object against MI355X's published peaks (2.5 PFLOP/s
+dense bf16 MFMA, 8 TB/s HBM3E).  ``cpu_baseline`` times the fp64 CPU oracle
+on the host on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def prefill_flops(B, Hq, S, D, causal=True):
+    pairs = S * (S + 1) // 2 if causal else S * S
+    return 4 * D * B * Hq * pairs
+
+
+def prefill_bytes(B, Hq, Hkv, S, D, elt=2):
+    return (B * Hq * S * D * 2 + B * Hkv * S * D * 2) * elt + B * Hq * S * 4
+
+
+def decode_bytes(seqlens, Hq, Hkv, D, elt=2):
+    kv = int(sum(int(x) for x in seqlens)) * Hkv * D * elt * 2
+    return kv + 2 * len(seqlens) * Hq * D * elt
+
+
+def cpu_baseline(wp, wd):
+    """Time the fp64 oracle on the host: the whole prefill workload once and
+    the whole decode workload once."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from causal_attention_amd import inputs
+
+    q, k, v = inputs.prefill_inputs(wp.B, wp.Hq, wp.Hkv, wp.S, wp.D,
+                                    wp.dtype, wp.sigma, wp.seed)
+    q, k, v = (t.float().numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, wp.scale, True)
+    tp = time.perf_counter() - t0
+    sl, q, kc, vc = inputs.workload_inputs(wd)
+    q, kc, vc = (t.float().numpy() for t in (q, kc, vc))
+    t0 = time.perf_counter()
+    oracle.decode(q, kc, vc, sl, wd.scale, wd.Hkv)
+    td = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": prefill_flops(wp.B, wp.Hq, wp.S, wp.D) / tp / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"whole prefill workload once ({tp:.2f} s) and whole "
+                   f"decode workload once ({td:.2f} s), numpy fp64"),
+        "decode_GBps": decode_bytes(sl, wd.Hq, wd.Hkv, wd.D) / td / 1e9,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="input copies cycled through (defeats the LLC)")
+    ap.add_argument("--prefill", default="c3_gqa_b4_s2048")
+    ap.add_argument("--decode", default="c4_decode_b32")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): this "
+              "path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_attention_amd import attn, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = inputs.WORKLOADS[args.prefill]
+    wd = inputs.WORKLOADS[args.decode]
+
+    q, k, v = inputs.prefill_inputs(wp.B, wp.Hq, wp.Hkv, wp.S, wp.D,
+                                    wp.dtype, wp.sigma, wp.seed)
+    sl, dq, kc, vc = inputs.workload_inputs(wd)
+    R = max(1, args.rotate)
+    P = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(R)]
+    Dd = [tuple(t.to(dev) for t in (dq, kc, vc)) for _ in range(R)]
+    sl_d = torch.from_numpy(sl).to(dev)
+    po = [torch.empty_like(P[0][0]) for _ in range(R)]
+    plse = [torch.empty((wp.B, wp.Hq, wp.S), dtype=torch.float32, device=dev)
+            for _ in range(R)]
+    do = [torch.empty_like(Dd[0][0]) for _ in range(R)]
+    ws = torch.empty(attn.attn_decode_workspace_size(
+        wd.B, wd.Hq, wd.Hkv, wd.D, args.num_splits), dtype=torch.uint8,
+        device=dev)
+    ns = args.num_splits or attn.attn_decode_auto_splits(wd.B, wd.Hkv)
+
+    def step(i, ev=None):
+        r = i % R
+        if ev is not None:
+            ev[0].record()
+        attn.attn_prefill(*P[r], causal=True, scale=wp.scale, out=po[r],
+                          lse=plse[r])
+        if ev is not None:
+            ev[1].record()
+        attn.attn_decode(*Dd[r], sl_d, Hkv=wd.Hkv, num_splits=ns,
+                         scale=wd.scale, out=do[r], workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pf_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dc_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pf_avg = sum(pf_ms) / K
+    dc_avg = sum(dc_ms) / K
+    flops = prefill_flops(wp.B, wp.Hq, wp.S, wp.D)
+    dbytes = decode_bytes(sl, wd.Hq, wd.Hkv, wd.D)
+    p_tflops = flops / (pf_avg * 1e-3) / 1e12
+    d_gbs = dbytes / (dc_avg * 1e-3) / 1e9
+
+    out = {
+        "metric": "prefill attention TFLOP/s + decode KV-cache GB/s, "
+                  "% of MI355X roofline",
+        "value": round(p_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wp.name} prefill + {wd.name} decode",
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "S": wp.S,
+                        "D": wp.D, "causal": True, "sigma": wp.sigma,
+                        "seed": wp.seed},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D,
+                       "seqlens": "U[256,4096] seed 0",
+                       "sum_seqlens": int(sl.sum()), "num_splits": ns},
+            "input_copies_rotated": R,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_prefill_bf16_kernel",
+            "achieved": round(p_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+            "avg_launch_us": round(pf_avg * 1e3, 3),
+        },
+        "decode": {
+            "value": round(d_gbs, 2),
+            "unit": "GB/s",
+            "avg_us": round(dc_avg * 1e3, 3),
+            "roofline": {
+                "bound": "hbm",
+                "kernel": "attn_decode_split_kernel + "
+                          "attn_decode_combine_kernel",
+                "achieved": round(d_gbs, 2),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                "traffic": None,
+                "bytes_per_launch": dbytes,
+            },
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wp, wd)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
