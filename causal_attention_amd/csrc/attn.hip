@@ -92,11 +92,11 @@ struct F32Prefill {
 // ------------------------------------------------------------------ decode
 
 int auto_splits(int B, int Hkv) {
-  // Aim for about 4096 split workgroups (16 per CU over 256 CUs) so the
-  // whole cache streams in roughly one wave of resident workgroups.
+  // Aim for about 2048 split workgroups (8 per CU over 256 CUs); a split is
+  // never shorter than 128 keys, so short sequences use fewer of them.
   const long long pairs = (long long)B * Hkv;
   if (pairs <= 0) return 1;
-  long long ns = (4096 + pairs - 1) / pairs;
+  long long ns = (2048 + pairs - 1) / pairs;
   if (ns < 1) ns = 1;
   if (ns > 128) ns = 128;
   return (int)ns;

@@ -17,6 +17,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Lazy rescaling of the online softmax: the running output is rescaled only
+// when a row max exceeds the reference by more than this many log2 units.
+constexpr float kLazyRescale = 8.f;
+
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.  Lane l holds
 // row (A) / column (B) l % 32 and eight contraction elements; C lane l holds
 // column l % 32, rows 8*(i/4) + 4*(l/32) + i%4 for i in 0..15.

@@ -7,31 +7,57 @@
 // running the online softmax of section 2.2, merged across blocks
 // afterwards), and the partial-buffer-plus-reduce-kernel pattern of
 // "手写Triton kernel重构Qwen3.5-0.8B" section 3.3 (a separate small reduce
-// kernel rather than atomics).  GQA (section 2.1 of that page): the Hq/Hkv
+// kernel rather than atomics).  GQA (section 2.1 of that page): the G = Hq/Hkv
 // query heads of one KV head are handled by the same workgroup, so each K/V
 // byte is read from HBM once, not once per query head.
 //
-// This path is bound by HBM bandwidth (about 4 FLOP per byte), so it uses no
-// MFMA.  A "lane group" of D/8 lanes owns one key row at a time, each lane
-// holding 8 dims loaded as one 16-byte vector, so one load instruction of a
-// wave covers 64/(D/8) consecutive key rows: one contiguous run of memory.  Each lane
-// group runs its own online softmax over its keys (the merge order does not
-// matter), so the loop has no cross-group communication; the groups are
-// merged once at the end of the split through LDS.  All loads of a batch of
-// UNR keys per group are issued before any arithmetic so that every lane
-// keeps 2*UNR 16-byte loads in flight.
+// gfx950 mapping.  The path is bound by HBM bandwidth (about 4 FLOP per
+// byte); the arithmetic is put on v_mfma_f32_16x16x32_bf16 only so that it
+// costs almost no issue slots next to the loads.  Each wave takes 32-key
+// blocks of its split:
+//  * S^T = K Q^T: the A operand is read straight from the cache (lane l holds
+//    key l%16 of a 16-key half, 8 consecutive dims), Q^T is the B operand with
+//    the G heads as columns (the other columns are zero).  The accumulator
+//    leaves lane l with head l%16 and keys 4*(l/16)..+3 of each half.
+//  * Those probabilities are re-used as the B operand of O^T = V^T P^T (key
+//    slot s of lane group l/16 is key 4*(l/16)+s of half 0 for s < 4, of half
+//    1 otherwise), so P never leaves registers.  V is read with coalesced
+//    16-byte loads and written transposed into a per-wave LDS tile, from which
+//    the A operand is two 8-byte reads per MFMA.
+//  * The row max and sum are per head, over the 4 lane groups: two cross-lane
+//    exchanges per block.  The running output is rescaled only when the max
+//    grows by more than 2^8 (exact: the final division by l cancels any
+//    common reference value; the bound keeps p <= 256).
+// The waves of a workgroup merge their (m, l, O) through LDS at the end, and
+// the split's normalised output and natural-log LSE go to the workspace.
 #pragma once
 
 #include "common.hpp"
 
 namespace attn {
 
-constexpr int kDecodeThreads = 128;    // 2 waves
-constexpr int kDecodeMinChunk = 64;    // smallest split, in keys
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kDecodeBlock = 32;                          // keys per wave step
+constexpr int kDecodeMinChunk = kDecodeWaves * kDecodeBlock;
 
-// Keys of split s for a sequence of L keys: [s*chunk, min(L, (s+1)*chunk)).
+// Keys of split s for a sequence of L keys: [s*chunk, min(L, (s+1)*chunk)),
+// chunk a multiple of 32 and at least one block per wave.
 __device__ __forceinline__ int decode_chunk(int L, int ns) {
-  return max((L + ns - 1) / ns, kDecodeMinChunk);
+  int c = max((L + ns - 1) / ns, kDecodeMinChunk);
+  return (c + kDecodeBlock - 1) / kDecodeBlock * kDecodeBlock;
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b,
+                                                    f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Wave-wide sum of a 64-bit value.
+__device__ __forceinline__ long long wave_sum64(long long x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
 }
 
 template <int D, int G>
@@ -40,151 +66,186 @@ __global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
     const __bf16* __restrict__ Vc, const int* __restrict__ seqlens,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hkv, int ns,
     float scale_log2) {
-  constexpr int GL = D / 8;                   // lanes per key row
-  constexpr int NG = kDecodeThreads / GL;     // lane groups per workgroup
-  constexpr int UNR = 8;                      // keys per group per batch
+  constexpr int KT = D / 32;          // QK k-steps (32 dims each)
+  constexpr int NDB = D / 16;         // PV output blocks (16 dims each)
+  constexpr int VSTR = kDecodeBlock + 4;   // V^T tile row stride (elements)
+  static_assert(G <= 16, "heads are MFMA columns");
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int Hq = Hkv * G;
-  const int L = max(seqlens[b], 0);
+
+  // L_b and the cache offset sum(L_0..L_{b-1}) from one load per lane.
+  long long prefix = 0;
+  int L = 0;
+  for (int base = 0; base <= b; base += 64) {
+    const int i = base + lane;
+    const int x = (i <= b) ? max(seqlens[i], 0) : 0;
+    if (b - base < 64) L = __shfl(x, b - base, 64);
+    prefix += wave_sum64(i < b ? x : 0);
+  }
   const int chunk = decode_chunk(L, ns);
   const long long start = (long long)s * chunk;
-  if (start >= L) return;                     // uniform over the workgroup
+  if (start >= L) return;                 // uniform over the workgroup
   const int kbeg = (int)start;
   const int kend = min(L, kbeg + chunk);
+  const __bf16* Kp = Kc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
+  const __bf16* Vp = Vc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
 
-  const int tid = threadIdx.x;
-  const int grp = tid / GL, gl = tid % GL;
+  // Q^T as the B operand: column c16 is head g*G + c16 (zero if c16 >= G),
+  // k-step t covers dims 32t + 8*g4 .. +7.
+  bf16x8 qB[KT];
+  const __bf16* qrow = Q + (size_t)(b * Hq + g * G + min(c16, G - 1)) * D;
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    qB[t] = (c16 < G) ? *reinterpret_cast<const bf16x8*>(qrow + 32 * t +
+                                                         8 * g4)
+                      : bf16x8{};
 
-  // Element offset of sequence b's cache block: Hkv*D*sum(L_0..L_{b-1}).
-  __shared__ long long red[kDecodeThreads / 64];
-  long long part = 0;
-  for (int i = tid; i < b; i += kDecodeThreads) part += max(seqlens[i], 0);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = part;
-  __syncthreads();
-  long long prefix = 0;
-#pragma unroll
-  for (int i = 0; i < kDecodeThreads / 64; ++i) prefix += red[i];
-  const size_t base =
-      ((size_t)prefix * Hkv + (size_t)g * L) * D + (size_t)gl * 8;
-  const __bf16* Kp = Kc + base;
-  const __bf16* Vp = Vc + base;
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[kDecodeWaves][D * VSTR];
+  __bf16* vt = Vt[w];
 
-  // This lane's 8 query dims of each head in the group, pre-scaled so the
-  // dot product is already a log2-domain score.
-  float q[G][8];
+  f32x4 oacc[NDB];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-        Q + ((size_t)(b * Hq + g * G + h)) * D + gl * 8);
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{};
+  float m_ref = -INFINITY;   // reference max (log2 domain) of head c16
+  float l_i = 0.f;           // lane-partial sum for head c16
+
+  for (int j0 = kbeg + w * kDecodeBlock; j0 < kend;
+       j0 += kDecodeWaves * kDecodeBlock) {
+    // --- loads: K as the A operand, V as coalesced rows (4 keys x 8 dims
+    // per lane and quad q).
+    bf16x8 ka[2][KT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q[h][2 * e] = bf16_lo(w4[e]) * scale_log2;
-      q[h][2 * e + 1] = bf16_hi(w4[e]) * scale_log2;
+    for (int kh = 0; kh < 2; ++kh) {
+      const int key = j0 + 16 * kh + c16;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        ka[kh][t] = (key < kend) ? *reinterpret_cast<const bf16x8*>(
+                                       Kp + (size_t)key * D + 32 * t + 8 * g4)
+                                 : bf16x8{};
     }
+    constexpr int VQ = kDecodeBlock / 16;     // key quads per lane
+    constexpr int VC = D / 8;                 // 16-byte chunks per row
+    static_assert(VC == 16 || VC == 8, "D = 128 or 64");
+    // lane -> (dim chunk, key quad): 16 lanes cover a 128-dim row; for D = 64
+    // the spare lanes take more quads.
+    constexpr int QPL = (kDecodeBlock / 4) / (64 / VC);   // quads per lane
+    u32x4 vr[QPL][4];
+#pragma unroll
+    for (int q = 0; q < QPL; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kq = lane / VC + (64 / VC) * q;
+        const int key = j0 + 4 * kq + i;
+        vr[q][i] = (key < kend) ? *reinterpret_cast<const u32x4*>(
+                                      Vp + (size_t)key * D + 8 * (lane % VC))
+                                : u32x4{};
+      }
+    (void)VQ;
+
+    // --- S^T = K Q^T
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      sacc[kh] = f32x4{};
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        sacc[kh] = mfma_16x16x32_bf16(ka[kh][t], qB[t], sacc[kh]);
+    }
+    // lane holds head c16, keys j0 + 16kh + 4g4 + i
+    float x[8];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + 16 * kh + 4 * g4 + i;
+        x[4 * kh + i] = (key < kend) ? sacc[kh][i] * scale_log2 : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > m_ref + kLazyRescale) {
+      // new reference (taken on the first block with a live key: m_ref is
+      // -inf there and the rescale factor is 0)
+      const float alpha = fast_exp2(m_ref - mx);
+      l_i *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+      m_ref = mx;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    bf16x8 pB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = fast_exp2(x[i] - m_use);
+      l_i += p;
+      pB[i] = (__bf16)p;
+    }
+
+    // --- V^T into this wave's LDS tile: dim e of keys 4kq..4kq+3 is one
+    // 8-byte run of row 8*(lane%VC) + e.
+#pragma unroll
+    for (int q = 0; q < QPL; ++q) {
+      const int kq = lane / VC + (64 / VC) * q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1, sh = (e & 1) * 16;
+        u32x2 pr;
+        pr[0] = ((vr[q][0][wd] >> sh) & 0xffffu) |
+                (((vr[q][1][wd] >> sh) & 0xffffu) << 16);
+        pr[1] = ((vr[q][2][wd] >> sh) & 0xffffu) |
+                (((vr[q][3][wd] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&vt[(8 * (lane % VC) + e) * VSTR + 4 * kq]) =
+            pr;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // --- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const __bf16* row = &vt[(16 * db + c16) * VSTR + 4 * g4];
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[db] = mfma_16x16x32_bf16(a, pB, oacc[db]);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  // Per-wave state of head c16: m_ref, l (sum over the 4 lane groups),
+  // O^T rows 16db + 4g4 + i.  Merge the waves through LDS.
+  l_i += __shfl_xor(l_i, 16, 64);
+  l_i += __shfl_xor(l_i, 32, 64);
+  __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
+  __shared__ float sm_o[kDecodeWaves][G][D];
+  if (g4 == 0) {
+    sm_m[w][c16] = m_ref;
+    sm_l[w][c16] = l_i;
   }
-
-  for (int k0 = kbeg; k0 < kend; k0 += NG * UNR) {
-    u32x4 kr[UNR], vr[UNR];
+  if (c16 < G) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int key = k0 + grp + NG * u;
-      if (key < kend) {
-        kr[u] = *reinterpret_cast<const u32x4*>(Kp + (size_t)key * D);
-        vr[u] = *reinterpret_cast<const u32x4*>(Vp + (size_t)key * D);
-      } else {
-        kr[u] = u32x4{};
-        vr[u] = u32x4{};
-      }
-    }
-    float sc[G][UNR];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf16_lo(kr[u][e]);
-        kf[2 * e + 1] = bf16_hi(kr[u][e]);
-      }
-      const bool ok = k0 + grp + NG * u < kend;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(q[h][e], kf[e], d);
-        d = group_sum<GL>(d);
-        sc[h][u] = ok ? d : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = sc[h][0];
-#pragma unroll
-      for (int u = 1; u < UNR; ++u) mx = fmaxf(mx, sc[h][u]);
-      const float m_new = fmaxf(m[h], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m[h] - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        sc[h][u] = fast_exp2(sc[h][u] - m_use);
-        psum += sc[h][u];
-      }
-      l[h] = l[h] * alpha + psum;
-      m[h] = m_new;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v0 = bf16_lo(vr[u][e]), v1 = bf16_hi(vr[u][e]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][2 * e] = fmaf(sc[h][u], v0, acc[h][2 * e]);
-          acc[h][2 * e + 1] = fmaf(sc[h][u], v1, acc[h][2 * e + 1]);
-        }
-      }
-    }
-  }
-
-  // Merge the NG lane groups of this workgroup (LSE algebra), then write
-  // this split's normalised output and natural-log LSE.
-  __shared__ float sm_m[NG][G], sm_l[NG][G];
-  __shared__ float sm_acc[NG][G][D];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm_acc[grp][h][gl * 8 + e] = acc[h][e];
-    if (gl == 0) {
-      sm_m[grp][h] = m[h];
-      sm_l[grp][h] = l[h];
-    }
+      for (int i = 0; i < 4; ++i) sm_o[w][c16][16 * db + 4 * g4 + i] =
+          oacc[db][i];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) M = fmaxf(M, sm_m[j][h]);
+    for (int j = 0; j < kDecodeWaves; ++j) M = fmaxf(M, sm_m[j][h]);
     float W = 0.f, o = 0.f;
 #pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const float wj = fast_exp2(sm_m[j][h] - M);   // 0 for an empty group
+    for (int j = 0; j < kDecodeWaves; ++j) {
+      const float wj = fast_exp2(sm_m[j][h] - M);   // 0 for an idle wave
       W = fmaf(wj, sm_l[j][h], W);
-      o = fmaf(wj, sm_acc[j][h][d], o);
+      o = fmaf(wj, sm_o[j][h][d], o);
     }
     const size_t row = ((size_t)(b * Hq + g * G + h)) * ns + s;
     ws_o[row * D + d] = o / W;
@@ -195,6 +256,8 @@ __global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
 // Combine the active splits of each (sequence, query head):
 // M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
 // lse = M + ln(sum w_s).  A sequence with no keys gives o = 0, lse = -inf.
+// One workgroup of D threads per (sequence, head); the split weights are
+// formed once in LDS and the partial rows are read 8 at a time.
 template <int D>
 __global__ __launch_bounds__(D) void attn_decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
@@ -209,13 +272,37 @@ __global__ __launch_bounds__(D) void attn_decode_combine_kernel(
   const float* lse_p = ws_lse + (size_t)bh * ns;
   const float* o_p = ws_o + (size_t)bh * ns * D;
 
-  float M = -INFINITY;
-  for (int s = 0; s < nact; ++s) M = fmaxf(M, lse_p[s]);
+  __shared__ float wgt[256];
+  __shared__ float red[D / 64];
+  float mloc = -INFINITY;
+  for (int s = d; s < nact; s += D) mloc = fmaxf(mloc, lse_p[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+  if ((d & 63) == 0) red[d >> 6] = mloc;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < D / 64; ++i) M = fmaxf(M, red[i]);
+  for (int s = d; s < nact; s += D)
+    wgt[s] = fast_exp2((lse_p[s] - M) * kLog2e);
+  __syncthreads();
+
   float W = 0.f, o = 0.f;
-  for (int s = 0; s < nact; ++s) {
-    const float w = fast_exp2((lse_p[s] - M) * kLog2e);
-    W += w;
-    o = fmaf(w, o_p[(size_t)s * D + d], o);
+  int s = 0;
+  for (; s + 8 <= nact; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = o_p[(size_t)(s + u) * D + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      W += wgt[s + u];
+      o = fmaf(wgt[s + u], v[u], o);
+    }
+  }
+  for (; s < nact; ++s) {
+    W += wgt[s];
+    o = fmaf(wgt[s], o_p[(size_t)s * D + d], o);
   }
   const float res = nact > 0 ? o / W : 0.f;
   O[(size_t)bh * D + d] = (__bf16)res;

@@ -53,20 +53,31 @@ __device__ __forceinline__ TileCoord tile_coord(int bid, int B, int Hq,
 }
 
 // Online-softmax update of one 32-query x (16*NKB)-key transposed score block
-// held as NKB accumulators.  x are log2-domain scores (masked = -inf).  Returns
-// alpha (the rescale factor of the old state) and overwrites x with p.
-template <int NKB>
-__device__ __forceinline__ float softmax_step(f32x16 (&x)[NKB], float& m_i,
-                                              float& l_i) {
+// held as NKB accumulators; x are log2-domain scores (masked = -inf) and are
+// overwritten with p = exp2(x - m_ref).  The running output is rescaled only
+// when the row max exceeds the reference m_ref by more than kLazyRescale
+// (2^8): the result is unchanged because the final division by l cancels any
+// common reference, and the bound keeps p <= 256 (finite in fp32, same
+// relative precision in bf16).  On the first visible block m_ref is -inf and
+// the rescale factor is 0.
+template <int NKB, int NDB>
+__device__ __forceinline__ void softmax_step(f32x16 (&x)[NKB], float& m_ref,
+                                             float& l_i, f32x16 (&oacc)[NDB]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[kb][i]);
   mx = fmaxf(mx, swap_halves(mx));
-  const float m_new = fmaxf(m_i, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(m_i - m_use);
+  if (mx > m_ref + kLazyRescale) {
+    const float alpha = fast_exp2(m_ref - mx);
+    l_i *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    m_ref = mx;
+  }
+  // A row with no visible key yet keeps m_ref = -inf and gets p = 0.
+  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
   float sum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -76,23 +87,22 @@ __device__ __forceinline__ float softmax_step(f32x16 (&x)[NKB], float& m_i,
       x[kb][i] = p;
       sum += p;
     }
-  l_i = l_i * alpha + sum;   // lane-partial: this half's keys only
-  m_i = m_new;
-  return alpha;
+  l_i += sum;   // lane-partial: this half's keys only
 }
 
-// Scale to the log2 domain and apply the causal / tail mask.  key(kb, i) is
-// the key index of accumulator element i of block kb for this lane.
-template <int NKB, bool CAUSAL>
+// Scale to the log2 domain and, when MASK, apply the causal / tail mask.
+// key(kb, i) is the key index of accumulator element i of block kb for this
+// lane (lane half hh).
+template <int NKB, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void scale_and_mask(f32x16 (&x)[NKB], float c,
                                                int j0, int hh, int query,
-                                               int S, bool need_mask) {
+                                               int S) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float v = x[kb][i] * c;
-      if (need_mask) {
+      if constexpr (MASK) {
         const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
         const bool dead = (key >= S) || (CAUSAL && key > query);
         v = dead ? -INFINITY : v;
@@ -102,24 +112,63 @@ __device__ __forceinline__ void scale_and_mask(f32x16 (&x)[NKB], float c,
 }
 
 // ---------------------------------------------------------------- bf16 path
+//
+// K and V tiles go global -> LDS with gfx950's direct loads
+// (global_load_lds_dwordx4: no VGPR staging, each wave instruction fills 1 KB
+// of LDS in lane order), double-buffered so that the next tile streams in
+// while the current one is multiplied; one barrier per tile.  Rows are
+// stored with their 16-byte chunks XOR-swizzled so the MFMA operand reads
+// hit distinct LDS banks.  V stays row-major in LDS and its transposed MFMA
+// operand comes from ds_read_b64_tr_b16: in each group of 16 lanes, lane j
+// points at 4 dims of key row j/4 and lane i receives dim i of those 4 keys.
+
+// LDS chunk position of 16-byte chunk c of row `row` (CPR chunks per row).
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row, int c) {
+  // A-operand reads: 16 consecutive rows, same chunk -> distinct banks.
+  return CPR == 16 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row, int c) {
+  // transposed reads: 4 consecutive rows x 4 aligned chunks -> distinct
+  // banks; XOR by a multiple of 4 keeps aligned chunk quads together.
+  return CPR == 16 ? (c ^ ((row & 3) << 2)) : (c ^ (((row >> 1) & 1) << 2));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ void lds_direct_load16(const void* g, __bf16* l) {
+  __builtin_amdgcn_global_load_lds(
+      g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPrefillThreads) void attn_prefill_bf16_kernel(
+__global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
     int n_qtiles) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
-  constexpr int KSTR = D + 8;                 // K tile row stride (elements)
-  constexpr int VSTR = BN + 4;                // V^T tile row stride
-  constexpr int DCH = D / 8;                  // 16-byte chunks per row
-  constexpr int KCH = BN * DCH / kPrefillThreads;      // K chunks per thread
-  constexpr int VTASKS = (BN / 4) * DCH;      // 4-key x 8-dim V blocks
-  static_assert(KCH >= 1 && VTASKS <= kPrefillThreads, "tile shape");
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per wave load instr
+  constexpr int IPW = BN / RPI / 4;           // load instrs per wave per tile
+  constexpr int TILE = BN * D;                // elements per K or V tile
+  static_assert(IPW >= 1, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VSTR];
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs1[TILE];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
@@ -151,86 +200,48 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_bf16_kernel(
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  // Global -> register staging of one K/V tile (prefetched one tile ahead).
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  const int vtask = tid;                       // valid if < VTASKS
-  const int vc = vtask % DCH, vkq = vtask / DCH;
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kPrefillThreads;
-      const int row = j0 + c / DCH, col = c % DCH;
-      kreg[i] = (row < S) ? *reinterpret_cast<const u32x4*>(
-                                Kp + (size_t)row * D + col * 8)
-                          : u32x4{};
-    }
-    if (vtask < VTASKS) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = j0 + 4 * vkq + u;
-        vreg[u] = (row < S) ? *reinterpret_cast<const u32x4*>(
-                                  Vp + (size_t)row * D + vc * 8)
-                            : u32x4{};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kPrefillThreads;
-      *reinterpret_cast<u32x4*>(&Ks[(c / DCH) * KSTR + (c % DCH) * 8]) =
-          kreg[i];
-    }
-    if (vtask < VTASKS) {
-      // Transpose a 4-key x 8-dim block: dim e of keys 4vkq..4vkq+3 becomes
-      // one 8-byte run of row (8vc + e) of V^T.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint32_t k0 = vreg[0][wd], k1 = vreg[1][wd], k2 = vreg[2][wd],
-                 k3 = vreg[3][wd];
-        if (e & 1) {
-          k0 >>= 16; k1 >>= 16; k2 >>= 16; k3 >>= 16;
-        }
-        u32x2 pr;
-        pr[0] = (k0 & 0xffffu) | (k1 << 16);
-        pr[1] = (k2 & 0xffffu) | (k3 << 16);
-        *reinterpret_cast<u32x2*>(&Vt[(8 * vc + e) * VSTR + 4 * vkq]) = pr;
-      }
-    }
-  };
-
-  if (n_kv > 0) load_tile(0);
-  for (int jt = 0; jt < n_kv; ++jt) {
+  // Issue the direct loads of key tile jt into (Kd, Vd).  Rows past the end
+  // of the sequence load row S-1 (their scores are masked to -inf, so their
+  // values are multiplied by p = 0).
+  auto issue_tile = [&](int jt, __bf16* Kd, __bf16* Vd) {
     const int j0 = jt * BN;
-    __syncthreads();              // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();              // tile visible to all waves
-    if (jt + 1 < n_kv) load_tile(j0 + BN);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r0 = (w * IPW + i) * RPI;
+      const int row = r0 + lane / CPR, pos = lane % CPR;
+      const size_t grow = (size_t)min(j0 + row, S - 1) * D;
+      lds_direct_load16(Kp + grow + 8 * swz_k<CPR>(row, pos), Kd + r0 * D);
+      lds_direct_load16(Vp + grow + 8 * swz_v<CPR>(row, pos), Vd + r0 * D);
+    }
+  };
 
-    // Waves whose rows all lie above this tile's first key skip it (all of
-    // its scores would be masked).
-    if (CAUSAL && j0 > wq0 + 31) continue;
-
+  auto compute_tile = [&](int j0, const __bf16* Kt, const __bf16* Vt) {
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = f32x16{};
+      const int row = kb * 32 + r;
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &Ks[(kb * 32 + r) * KSTR + 16 * t + 8 * hh]);
+            Kt + row * D + 8 * swz_k<CPR>(row, 2 * t + hh));
         sacc[kb] = mfma_32x32x16_bf16(a, qB[t], sacc[kb]);
       }
     }
-    const bool need_mask = (j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0);
-    scale_and_mask<NKB, CAUSAL>(sacc, scale_log2, j0, hh, query, S,
-                                need_mask);
-    const float alpha = softmax_step<NKB>(sacc, m_i, l_i);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    // Only the diagonal and the ragged tail tiles need the elementwise mask
+    // (a wave-uniform choice).
+    if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
+      scale_and_mask<NKB, CAUSAL, true>(sacc, scale_log2, j0, hh, query, S);
+    else
+      scale_and_mask<NKB, CAUSAL, false>(sacc, scale_log2, j0, hh, query, S);
+    softmax_step<NKB, NDB>(sacc, m_i, l_i, oacc);
 
+    // O^T += V^T P^T.  Lane group G = lane/16 reads dims 16*(G%2) of the
+    // 32-dim block and keys 4*(G/2) (+8) of the 16-key step, matching the
+    // key order of P^T in the B operand.
+    const int grp = lane >> 4, j = lane & 15;
+    const int vrow_off = 4 * (grp >> 1) + (j >> 2);
+    const int vcol_off = 16 * (grp & 1) + 4 * (j & 3);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -238,21 +249,39 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_bf16_kernel(
         bf16x8 pb;
 #pragma unroll
         for (int s = 0; s < 8; ++s) pb[s] = (__bf16)sacc[kb][8 * u + s];
-        // Slot s of this lane holds key kb*32 + 16u + 4hh + (s&3) + 8*(s>>2).
-        const int kcol = kb * 32 + 16 * u + 4 * hh;
+        const int row0 = kb * 32 + 16 * u + vrow_off;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const __bf16* vrow = &Vt[(db * 32 + r) * VSTR + kcol];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
+          const int col = db * 32 + vcol_off;
+          const int c = col >> 3, e = col & 7;
+          const bf16x4 lo = lds_read_tr16(Vt + row0 * D +
+                                          8 * swz_v<CPR>(row0, c) + e);
+          const bf16x4 hi = lds_read_tr16(Vt + (row0 + 8) * D +
+                                          8 * swz_v<CPR>(row0 + 8, c) + e);
           const bf16x8 a = {lo[0], lo[1], lo[2], lo[3],
                             hi[0], hi[1], hi[2], hi[3]};
           oacc[db] = mfma_32x32x16_bf16(a, pb, oacc[db]);
         }
       }
+  };
+
+  if (n_kv > 0) issue_tile(0, Ks0, Vs0);
+  for (int jt = 0; jt < n_kv; ++jt) {
+    const int j0 = jt * BN;
+    wait_vmem();                  // this wave's loads of tile jt landed
+    __syncthreads();              // everyone's landed; tile jt-1 consumed
+    const bool odd = jt & 1;
+    if (jt + 1 < n_kv) {
+      if (odd) issue_tile(jt + 1, Ks0, Vs0);
+      else issue_tile(jt + 1, Ks1, Vs1);
+    }
+    // Waves whose rows all lie above this tile's first key skip it.
+    if (CAUSAL && j0 > wq0 + 31) continue;
+    if (odd) compute_tile(j0, Ks1, Vs1);
+    else compute_tile(j0, Ks0, Vs0);
   }
 
-  // Epilogue: O = acc / l (bf16, RNE) and LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = acc / l (bf16, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
   if (query < S) {
     const float inv = 1.f / l_tot;
@@ -375,12 +404,11 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
         sacc[kb] = mfma_32x32x2_f32(a4[3], qB[t + 3], sacc[kb]);
       }
     }
-    const bool need_mask = (j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0);
-    scale_and_mask<NKB, CAUSAL>(sacc, scale_log2, j0, hh, query, S,
-                                need_mask);
-    const float alpha = softmax_step<NKB>(sacc, m_i, l_i);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
+      scale_and_mask<NKB, CAUSAL, true>(sacc, scale_log2, j0, hh, query, S);
+    else
+      scale_and_mask<NKB, CAUSAL, false>(sacc, scale_log2, j0, hh, query, S);
+    softmax_step<NKB, NDB>(sacc, m_i, l_i, oacc);
 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
