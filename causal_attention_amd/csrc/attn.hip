@@ -27,7 +27,7 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o,
   if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0) return ATTN_ERR_SHAPE;
   if (Hq == 0 || Hkv == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
   // Grid size: one workgroup per (batch, query head, 128-row tile).
   const long long tiles = ((long long)S + kPrefillBM - 1) / kPrefillBM;
   if ((long long)B * Hq * tiles > 0x7fffffffLL) return ATTN_ERR_SHAPE;
@@ -197,7 +197,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
                 size_t workspace_bytes, void* stream) {
   int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
   if (st != ATTN_OK) return st;
-  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
   if (B == 0) return ATTN_OK;
   if (!q || !kcache || !vcache || !seqlens || !o || !workspace)
     return ATTN_ERR_NULL;

@@ -18,7 +18,8 @@
 // over keys accepts any key order, as long as the A operand V^T reads V in the
 // same order), so P never leaves registers.  V is stored transposed in LDS so
 // that each lane's eight keys for one output dimension are two 8-byte runs.
-// Softmax runs in the exp2 domain with scale*log2(e) folded in.
+// Softmax runs in the exp2 domain with scale*log2(e) folded into the exp2
+// argument (the scale must be positive).
 #pragma once
 
 #include "common.hpp"
@@ -53,22 +54,26 @@ __device__ __forceinline__ TileCoord tile_coord(int bid, int B, int Hq,
 }
 
 // Online-softmax update of one 32-query x (16*NKB)-key transposed score block
-// held as NKB accumulators; x are log2-domain scores (masked = -inf) and are
-// overwritten with p = exp2(x - m_ref).  The running output is rescaled only
-// when the row max exceeds the reference m_ref by more than kLazyRescale
-// (2^8): the result is unchanged because the final division by l cancels any
-// common reference, and the bound keeps p <= 256 (finite in fp32, same
-// relative precision in bf16).  On the first visible block m_ref is -inf and
-// the rescale factor is 0.
+// held as NKB accumulators of RAW scores q.k (masked = -inf).  With
+// c = scale*log2(e) > 0 the log2-domain score is x*c, so the row max is taken
+// on the raw scores and the scale is folded into the exp2 argument
+// (p = exp2(x*c - m_ref), one FMA per score); x is overwritten with p.
+//
+// The running output is rescaled only when the row max exceeds the
+// reference m_ref by more than kLazyRescale (2^8): the result is unchanged
+// because the final division by l cancels any common reference, and the
+// bound keeps p <= 256 (finite in fp32, same relative precision in bf16).  On
+// the first visible block m_ref is -inf and the rescale factor is 0.
 template <int NKB, int NDB>
-__device__ __forceinline__ void softmax_step(f32x16 (&x)[NKB], float& m_ref,
-                                             float& l_i, f32x16 (&oacc)[NDB]) {
+__device__ __forceinline__ void softmax_step(f32x16 (&x)[NKB], float c,
+                                             float& m_ref, float& l_i,
+                                             f32x16 (&oacc)[NDB]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[kb][i]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = fmaxf(mx, swap_halves(mx)) * c;
   if (mx > m_ref + kLazyRescale) {
     const float alpha = fast_exp2(m_ref - mx);
     l_i *= alpha;
@@ -77,37 +82,31 @@ __device__ __forceinline__ void softmax_step(f32x16 (&x)[NKB], float& m_ref,
     m_ref = mx;
   }
   // A row with no visible key yet keeps m_ref = -inf and gets p = 0.
-  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
   float sum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(x[kb][i] - m_use);
+      const float p = fast_exp2(fmaf(x[kb][i], c, neg_m));
       x[kb][i] = p;
       sum += p;
     }
   l_i += sum;   // lane-partial: this half's keys only
 }
 
-// Scale to the log2 domain and, when MASK, apply the causal / tail mask.
-// key(kb, i) is the key index of accumulator element i of block kb for this
-// lane (lane half hh).
-template <int NKB, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void scale_and_mask(f32x16 (&x)[NKB], float c,
-                                               int j0, int hh, int query,
-                                               int S) {
+// Causal / tail mask of a raw score block: key(kb, i) is the key index of
+// accumulator element i of block kb for this lane (lane half hh).
+template <int NKB, bool CAUSAL>
+__device__ __forceinline__ void apply_mask(f32x16 (&x)[NKB], int j0, int hh,
+                                           int query, int S) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float v = x[kb][i] * c;
-      if constexpr (MASK) {
-        const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const bool dead = (key >= S) || (CAUSAL && key > query);
-        v = dead ? -INFINITY : v;
-      }
-      x[kb][i] = v;
+      const int key = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      const bool dead = (key >= S) || (CAUSAL && key > query);
+      x[kb][i] = dead ? -INFINITY : x[kb][i];
     }
 }
 
@@ -165,13 +164,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   constexpr int TILE = BN * D;                // elements per K or V tile
   static_assert(IPW >= 1, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) __bf16 Ks0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vs0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Ks1[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vs1[TILE];
+  // [buffer][K, V][TILE]
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * TILE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  // wave index as a uniform (scalar) value, so per-wave branches are scalar
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const TileCoord tc = tile_coord(blockIdx.x, B, Hq, Hkv, n_qtiles);
   const __bf16* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
   const __bf16* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
@@ -229,12 +228,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
       }
     }
     // Only the diagonal and the ragged tail tiles need the elementwise mask
-    // (a wave-uniform choice).
+    // (a wave-uniform, scalar branch).
     if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
-      scale_and_mask<NKB, CAUSAL, true>(sacc, scale_log2, j0, hh, query, S);
-    else
-      scale_and_mask<NKB, CAUSAL, false>(sacc, scale_log2, j0, hh, query, S);
-    softmax_step<NKB, NDB>(sacc, m_i, l_i, oacc);
+      apply_mask<NKB, CAUSAL>(sacc, j0, hh, query, S);
+    softmax_step<NKB, NDB>(sacc, scale_log2, m_i, l_i, oacc);
 
     // O^T += V^T P^T.  Lane group G = lane/16 reads dims 16*(G%2) of the
     // 32-dim block and keys 4*(G/2) (+8) of the 16-key step, matching the
@@ -265,20 +262,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
       }
   };
 
-  if (n_kv > 0) issue_tile(0, Ks0, Vs0);
+  // Tile jt lives in buffer jt & 1.  Every wave computes every tile of the
+  // workgroup's range: a wave whose rows all lie above a tile's first keys
+  // gets p = 0 from the mask (skipping it with a branch would make the
+  // compiler copy the accumulator registers on every tile).
+  if (n_kv > 0) issue_tile(0, smem, smem + TILE);
   for (int jt = 0; jt < n_kv; ++jt) {
-    const int j0 = jt * BN;
     wait_vmem();                  // this wave's loads of tile jt landed
     __syncthreads();              // everyone's landed; tile jt-1 consumed
-    const bool odd = jt & 1;
-    if (jt + 1 < n_kv) {
-      if (odd) issue_tile(jt + 1, Ks0, Vs0);
-      else issue_tile(jt + 1, Ks1, Vs1);
-    }
-    // Waves whose rows all lie above this tile's first key skip it.
-    if (CAUSAL && j0 > wq0 + 31) continue;
-    if (odd) compute_tile(j0, Ks1, Vs1);
-    else compute_tile(j0, Ks0, Vs0);
+    __bf16* cur = smem + (jt & 1) * 2 * TILE;
+    __bf16* nxt = smem + ((jt + 1) & 1) * 2 * TILE;
+    if (jt + 1 < n_kv) issue_tile(jt + 1, nxt, nxt + TILE);
+    compute_tile(jt * BN, cur, cur + TILE);
   }
 
   // Epilogue: O = acc / l (bf16, RNE) and LSE = (m_ref + log2 l) * ln 2.
@@ -328,7 +323,8 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
   __shared__ __attribute__((aligned(16))) float Vs[BN * STR];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const TileCoord tc = tile_coord(blockIdx.x, B, Hq, Hkv, n_qtiles);
   const float* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
   const float* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
@@ -405,10 +401,8 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
       }
     }
     if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
-      scale_and_mask<NKB, CAUSAL, true>(sacc, scale_log2, j0, hh, query, S);
-    else
-      scale_and_mask<NKB, CAUSAL, false>(sacc, scale_log2, j0, hh, query, S);
-    softmax_step<NKB, NDB>(sacc, m_i, l_i, oacc);
+      apply_mask<NKB, CAUSAL>(sacc, j0, hh, query, S);
+    softmax_step<NKB, NDB>(sacc, scale_log2, m_i, l_i, oacc);
 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)

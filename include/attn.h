@@ -48,7 +48,7 @@ typedef enum {
   ATTN_ERR_WORKSPACE = -6, /* decode workspace smaller than required */
   ATTN_ERR_SPLITS = -7,    /* num_splits < 0 or > ATTN_MAX_SPLITS */
   ATTN_ERR_LAUNCH = -8,    /* the HIP runtime rejected a kernel launch */
-  ATTN_ERR_SCALE = -9      /* scale is not a finite number */
+  ATTN_ERR_SCALE = -9      /* scale is not a finite positive number */
 } attn_status;
 
 /* Largest num_splits attn_decode accepts. */
@@ -61,9 +61,9 @@ typedef enum {
  *                                   masked score row (m + ln l; the form of
  *                                   the "triton-optimization" page, section
  *                                   3.5); may be NULL to skip it.
- *   scale: multiplier of Q K^T (1/sqrt(D) in the usual setting; the fused
- *          Triton kernel of the attention-fusion page, section 3.2, applies it
- *          to qk before the softmax).
+ *   scale: multiplier of Q K^T, finite and > 0 (1/sqrt(D) in the usual
+ *          setting; the fused Triton kernel of the attention-fusion page,
+ *          section 3.2, applies it to qk before the softmax).
  *   causal: nonzero for the causal mask j <= i, zero for no mask.
  * Any S >= 0 is accepted (tail tiles are masked, as section 6.1 of the
  * attention-fusion page requires).  D must be 64 or 128.
@@ -110,6 +110,7 @@ int attn_decode_auto_splits(int B, int Hkv);
  *   num_splits: key chunks per sequence, 1..ATTN_MAX_SPLITS, or 0 for
  *              attn_decode_auto_splits(B, Hkv).  A sequence is cut into at
  *              most num_splits chunks of at least 64 keys.
+ *   scale    : multiplier of q.k, finite and > 0.
  *   lse      : [B, Hq] fp32 natural-log LSE, or NULL.
  *   workspace: DEVICE scratch of at least
  *              attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) bytes,

@@ -63,6 +63,8 @@ def test_prefill_argument_errors(fn):
     assert prefill(fn, lse=A + 2) == -5
     assert prefill(fn, scale=float("nan")) == -9
     assert prefill(fn, scale=float("inf")) == -9
+    assert prefill(fn, scale=0.0) == -9
+    assert prefill(fn, scale=-0.125) == -9
     # grid too large for one launch
     assert prefill(fn, B=65536, Hq=1024, Hkv=1, S=1 << 20) == -2
 
@@ -95,6 +97,7 @@ def test_decode_argument_errors():
     assert decode(ws=A + 4) == -5
     assert decode(wsb=100) == -6
     assert decode(scale=float("nan")) == -9
+    assert decode(scale=-1.0) == -9
     assert decode(B=0, q=None, kc=None, vc=None, sl=None, o=None, ws=None) == 0
 
 
