@@ -117,21 +117,26 @@ def main():
     plse = [torch.empty((wp.B, wp.Hq, wp.S), dtype=torch.float32, device=dev)
             for _ in range(R)]
     do = [torch.empty_like(Dd[0][0]) for _ in range(R)]
-    ws = torch.empty(attn.attn_decode_workspace_size(
-        wd.B, wd.Hq, wd.Hkv, wd.D, args.num_splits), dtype=torch.uint8,
-        device=dev)
+    ws = attn.new_decode_workspace(wd.B, wd.Hq, wd.Hkv, wd.D,
+                                   args.num_splits, dev)
     ns = args.num_splits or attn.attn_decode_auto_splits(wd.B, wd.Hkv)
+
+    # Arguments are converted once; each launch is then a single C call, so
+    # the host stays ahead of the GPU and the events time the kernels.
+    pre = [attn.prepare_prefill(*P[r], po[r], plse[r], causal=True,
+                                scale=wp.scale) for r in range(R)]
+    dec = [attn.prepare_decode(*Dd[r], sl_d, do[r], wd.Hkv, ws,
+                               num_splits=ns, scale=wd.scale)
+           for r in range(R)]
 
     def step(i, ev=None):
         r = i % R
         if ev is not None:
             ev[0].record()
-        attn.attn_prefill(*P[r], causal=True, scale=wp.scale, out=po[r],
-                          lse=plse[r])
+        pre[r]()
         if ev is not None:
             ev[1].record()
-        attn.attn_decode(*Dd[r], sl_d, Hkv=wd.Hkv, num_splits=ns,
-                         scale=wd.scale, out=do[r], workspace=ws)
+        dec[r]()
         if ev is not None:
             ev[2].record()
 

@@ -137,14 +137,20 @@ def attn_decode_workspace_size(B, Hq, Hkv, D, num_splits=0):
     return n
 
 
+def new_decode_workspace(B, Hq, Hkv, D, num_splits=0, device="cuda"):
+    """A workspace for attn_decode (reusable by calls on one stream)."""
+    need = attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) if B else 0
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
                 out=None, with_lse=False, lse=None, workspace=None):
     """Split-K decode attention over a packed per-sequence KV cache.
 
     q [B,Hq,D] bf16; kcache, vcache flat bf16 caches where sequence b is a
     [Hkv, L_b, D] block; seqlens int32 [B] on the GPU.  Returns (o, lse);
-    lse is fp32 [B,Hq] or None.  ``workspace`` (uint8 GPU tensor) is
-    allocated when not given.
+    lse is fp32 [B,Hq] or None.  ``workspace`` (uint8 GPU tensor, see
+    ``new_decode_workspace``) is allocated when not given.
     """
     _check(q, "q", torch.bfloat16, 3)
     _check(kcache, "kcache", torch.bfloat16, None)
@@ -166,8 +172,7 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
         _check(lse, "lse", torch.float32, 2)
     need = attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) if B else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
-                                device=q.device)
+        workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
     _check(workspace, "workspace", torch.uint8, 1)
     st = lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens),
                            _ptr(out), B, Hq, Hkv, D, float(scale),
@@ -176,3 +181,67 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
     if st != 0:
         raise AttnError(st, "attn_decode")
     return out, lse
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments validated and converted once.
+
+    Calling the object issues a single ctypes call: no checks, no
+    allocation, no stream lookup.  It keeps its tensors alive; the caller
+    must not resize or free them while the object is in use.  Meant for
+    timing loops and serving loops where per-call Python work would
+    otherwise outlast the kernels.
+    """
+
+    def __init__(self, fn, name, args, keep):
+        self._fn, self._name, self._args, self._keep = fn, name, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise AttnError(st, self._name)
+
+
+def prepare_prefill(q, k, v, out, lse=None, causal=True, scale=None):
+    """A PreparedCall of attn_prefill / attn_prefill_f32 on the current
+    stream (arguments as for ``attn_prefill``; ``out`` is required)."""
+    dtype = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _check(t, n, dtype, 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or out.shape != q.shape:
+        raise ValueError("inconsistent prefill shapes")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if lse.shape != (B, Hq, S):
+            raise ValueError("lse must be [B,Hq,S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    fn = lib().attn_prefill if dtype == torch.bfloat16 else \
+        lib().attn_prefill_f32
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
+            D, ctypes.c_float(scale), int(bool(causal)), _stream())
+    return PreparedCall(fn, fn.__name__, args, (q, k, v, out, lse))
+
+
+def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
+                   num_splits=0, lse=None, scale=None):
+    """A PreparedCall of attn_decode on the current stream (arguments as for
+    ``attn_decode``; ``out`` and ``workspace`` are required)."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(kcache, "kcache", torch.bfloat16, None)
+    _check(vcache, "vcache", torch.bfloat16, None)
+    _check(seqlens, "seqlens", torch.int32, 1)
+    _check(out, "out", torch.bfloat16, 3)
+    _check(workspace, "workspace", torch.uint8, 1)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    args = (_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B,
+            Hq, Hkv, D, ctypes.c_float(scale), int(num_splits), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream())
+    return PreparedCall(lib().attn_decode, "attn_decode", args,
+                        (q, kcache, vcache, seqlens, out, workspace, lse))

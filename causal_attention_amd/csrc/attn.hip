@@ -92,13 +92,15 @@ struct F32Prefill {
 // ------------------------------------------------------------------ decode
 
 int auto_splits(int B, int Hkv) {
-  // Aim for about 2048 split workgroups (8 per CU over 256 CUs); a split is
-  // never shorter than 128 keys, so short sequences use fewer of them.
+  // Splits are at least 128 keys (one 32-key block per wave of a 4-wave
+  // workgroup).  Allow enough of them that short batches still fill the
+  // GPU (about 2048 workgroups), and at least 32 so caches up to 4096 keys
+  // are cut into 128-key chunks.
   const long long pairs = (long long)B * Hkv;
-  if (pairs <= 0) return 1;
+  if (pairs <= 0) return 32;
   long long ns = (2048 + pairs - 1) / pairs;
-  if (ns < 1) ns = 1;
-  if (ns > 128) ns = 128;
+  if (ns < 32) ns = 32;
+  if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
   return (int)ns;
 }
 
@@ -114,13 +116,20 @@ int check_decode_sizes(int B, int Hq, int Hkv, int D, int num_splits) {
   return ATTN_OK;
 }
 
-size_t workspace_bytes_for(int B, int Hq, int D, int ns) {
-  // fp32 partial outputs [B, Hq, ns, D] followed by partial LSEs [B, Hq, ns],
-  // the LSE block starting on a 16-byte boundary.
+// Workspace layout: fp32 partial outputs [B, Hq, ns, D], then fp32 partial
+// LSEs [B, Hq, ns], each starting on a 16-byte boundary.
+struct DecodeWorkspace {
+  size_t o_off, lse_off, bytes;
+};
+
+DecodeWorkspace decode_workspace(int B, int Hq, int D, int ns) {
+  auto up16 = [](size_t x) { return (x + 15) / 16 * 16; };
   const size_t rows = (size_t)B * Hq * ns;
-  size_t o_bytes = rows * D * sizeof(float);
-  o_bytes = (o_bytes + 15) / 16 * 16;
-  return o_bytes + rows * sizeof(float);
+  DecodeWorkspace w;
+  w.o_off = 0;
+  w.lse_off = up16(rows * D * sizeof(float));
+  w.bytes = w.lse_off + up16(rows * sizeof(float));
+  return w;
 }
 
 template <int D, int G>
@@ -188,7 +197,7 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
                                   int num_splits) {
   if (check_decode_sizes(B, Hq, Hkv, D, num_splits) != ATTN_OK) return 0;
   const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
-  return workspace_bytes_for(B, Hq, D, ns);
+  return decode_workspace(B, Hq, D, ns).bytes;
 }
 
 int attn_decode(const void* q, const void* kcache, const void* vcache,
@@ -206,13 +215,12 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
       !aligned(workspace, 16))
     return ATTN_ERR_ALIGN;
   const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
-  if (workspace_bytes < workspace_bytes_for(B, Hq, D, ns))
-    return ATTN_ERR_WORKSPACE;
+  const DecodeWorkspace wl = decode_workspace(B, Hq, D, ns);
+  if (workspace_bytes < wl.bytes) return ATTN_ERR_WORKSPACE;
 
-  const size_t rows = (size_t)B * Hq * ns;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = reinterpret_cast<float*>(
-      static_cast<char*>(workspace) + (rows * D * sizeof(float) + 15) / 16 * 16);
+  char* ws = static_cast<char*>(workspace);
+  float* ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+  float* ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
   const int G = Hq / Hkv;
   const float sl2 = scale * attn::kLog2e;
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -221,8 +229,8 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
   const __bf16* vb = static_cast<const __bf16*>(vcache);
   __bf16* ob = static_cast<__bf16*>(o);
   if (D == 64)
-    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B, Hkv,
-                        ns, sl2, hs);
+    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B,
+                        Hkv, ns, sl2, hs);
   else
     launch_decode_d<128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B,
                          Hkv, ns, sl2, hs);

@@ -14,22 +14,28 @@
 // gfx950 mapping.  The path is bound by HBM bandwidth (about 4 FLOP per
 // byte); the arithmetic is put on v_mfma_f32_16x16x32_bf16 only so that it
 // costs almost no issue slots next to the loads.  Each wave takes 32-key
-// blocks of its split:
-//  * S^T = K Q^T: the A operand is read straight from the cache (lane l holds
-//    key l%16 of a 16-key half, 8 consecutive dims), Q^T is the B operand with
-//    the G heads as columns (the other columns are zero).  The accumulator
-//    leaves lane l with head l%16 and keys 4*(l/16)..+3 of each half.
+// blocks of its split and keeps the next block's loads in flight while it
+// multiplies the current one:
+//  * S^T = K Q^T: the A operand is read straight from the cache into VGPRs
+//    (lane l holds key l%16 of a 16-key half, 8 consecutive dims), Q^T is the
+//    B operand with the G heads as columns (the other columns are zero).  The
+//    accumulator leaves lane l with head l%16 and keys 4*(l/16)..+3 of each
+//    half.
 //  * Those probabilities are re-used as the B operand of O^T = V^T P^T (key
 //    slot s of lane group l/16 is key 4*(l/16)+s of half 0 for s < 4, of half
-//    1 otherwise), so P never leaves registers.  V is read with coalesced
-//    16-byte loads and written transposed into a per-wave LDS tile, from which
-//    the A operand is two 8-byte reads per MFMA.
+//    1 otherwise), so P never leaves registers.  V goes global -> LDS with
+//    gfx950's direct loads into a per-wave double buffer, and the A operand
+//    V^T comes from transposed LDS reads (ds_read_b64_tr_b16).
 //  * The row max and sum are per head, over the 4 lane groups: two cross-lane
 //    exchanges per block.  The running output is rescaled only when the max
 //    grows by more than 2^8 (exact: the final division by l cancels any
 //    common reference value; the bound keeps p <= 256).
-// The waves of a workgroup merge their (m, l, O) through LDS at the end, and
-// the split's normalised output and natural-log LSE go to the workspace.
+// The waves of a workgroup merge their (m, l, O) through LDS at the end and
+// write the split's normalised output and natural-log LSE to the workspace;
+// a second small kernel merges the splits of each (sequence, head).  (Doing
+// that merge in the last split to finish would need device-scope fences,
+// which on this 8-XCD part write back and invalidate a whole L2 per
+// workgroup: far slower than one more launch.)
 #pragma once
 
 #include "common.hpp"
@@ -60,19 +66,155 @@ __device__ __forceinline__ long long wave_sum64(long long x) {
   return x;
 }
 
+// Direct global -> LDS load of 16 bytes per lane (lane order in LDS) and
+// the transposed LDS read (in each group of 16 lanes, lane j points at 4
+// dims of key row j/4; lane i receives dim i of those 4 keys).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dec_lds_load16(const void* g, __bf16* l) {
+  __builtin_amdgcn_global_load_lds(
+      g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+__device__ __forceinline__ bf16x4 dec_lds_read_tr16(const __bf16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// V block rows in LDS: 16-byte chunk c of key row r is stored at chunk
+// position c ^ f(r), so the 16 rows read by one transposed load hit distinct
+// banks (f is even, which keeps chunk pairs together).
+template <int D>
+__device__ __forceinline__ int dec_swz(int row, int c) {
+  return D == 128 ? (c ^ ((row & 7) << 1)) : (c ^ (((row >> 1) & 3) << 1));
+}
+
+// One 32-key block of one wave: K in registers as two 16-key MFMA A
+// operands; V goes straight to the wave's LDS buffer.
+template <int D>
+struct DecodeK {
+  bf16x8 ka[2][D / 32];
+};
+
+// Issue the loads of the block at key j0 (keys >= kend: K reads as zero,
+// V rows clamp to the last live key and are multiplied by p = 0).
+template <int D>
+__device__ __forceinline__ void decode_load(DecodeK<D>& blk, __bf16* vdst,
+                                            const __bf16* Kp,
+                                            const __bf16* Vp, int j0,
+                                            int kend, int lane) {
+  constexpr int KT = D / 32;
+  constexpr int CPR = D / 8;                 // chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per load instruction
+  const int c16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int key = j0 + 16 * kh + c16;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      blk.ka[kh][t] = (key < kend) ? *reinterpret_cast<const bf16x8*>(
+                                         Kp + (size_t)key * D + 32 * t + 8 * g4)
+                                   : bf16x8{};
+  }
+#pragma unroll
+  for (int i = 0; i < kDecodeBlock / RPI; ++i) {
+    const int row = i * RPI + lane / CPR, pos = lane % CPR;
+    const int key = min(j0 + row, kend - 1);
+    dec_lds_load16(Vp + (size_t)key * D + 8 * dec_swz<D>(row, pos),
+                   vdst + i * RPI * D);
+  }
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Online-softmax step of one wave over one 32-key block whose V rows are in
+// vsrc (its loads are the only ones this wave has in flight).
+template <int D>
+__device__ __forceinline__ void decode_step(const DecodeK<D>& blk,
+                                            const bf16x8 (&qB)[D / 32],
+                                            const __bf16* vsrc, int j0,
+                                            int kend, int lane, float c,
+                                            float& m_ref, float& l_i,
+                                            f32x4 (&oacc)[D / 16]) {
+  constexpr int KT = D / 32;
+  constexpr int NDB = D / 16;
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  f32x4 sacc[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    sacc[kh] = f32x4{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      sacc[kh] = mfma_16x16x32_bf16(blk.ka[kh][t], qB[t], sacc[kh]);
+  }
+  // lane holds head c16, keys j0 + 16kh + 4g4 + i (raw q.k; masked = -inf)
+  float x[8];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = j0 + 16 * kh + 4 * g4 + i;
+      x[4 * kh + i] = (key < kend) ? sacc[kh][i] : -INFINITY;
+    }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+  if (mx > m_ref + kLazyRescale) {
+    // new reference (taken on the first block with a live key: m_ref is
+    // -inf there and the rescale factor is 0)
+    const float alpha = fast_exp2(m_ref - mx);
+    l_i *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+    m_ref = mx;
+  }
+  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+  bf16x8 pB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = fast_exp2(fmaf(x[i], c, neg_m));
+    l_i += p;
+    pB[i] = (__bf16)p;
+  }
+
+  wait_vmem_le<0>();               // this block's V rows have landed
+  // O^T += V^T P^T: lane group g4 reads keys 4g4..+3 and 16+4g4..+3 (the
+  // key order of P^T), dims 16db + (lane & 15).
+  const int r0 = 4 * g4 + (c16 >> 2);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = 16 * db + 4 * (c16 & 3);
+    const int ch = col >> 3, e = col & 7;
+    const bf16x4 lo = dec_lds_read_tr16(vsrc + r0 * D +
+                                        8 * dec_swz<D>(r0, ch) + e);
+    const bf16x4 hi = dec_lds_read_tr16(vsrc + (r0 + 16) * D +
+                                        8 * dec_swz<D>(r0 + 16, ch) + e);
+    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    oacc[db] = mfma_16x16x32_bf16(a, pB, oacc[db]);
+  }
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads, 4) void attn_decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     const __bf16* __restrict__ Vc, const int* __restrict__ seqlens,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hkv, int ns,
     float scale_log2) {
   constexpr int KT = D / 32;          // QK k-steps (32 dims each)
   constexpr int NDB = D / 16;         // PV output blocks (16 dims each)
-  constexpr int VSTR = kDecodeBlock + 4;   // V^T tile row stride (elements)
   static_assert(G <= 16, "heads are MFMA columns");
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
   const int Hq = Hkv * G;
 
@@ -86,9 +228,9 @@ __global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
     prefix += wave_sum64(i < b ? x : 0);
   }
   const int chunk = decode_chunk(L, ns);
-  const long long start = (long long)s * chunk;
-  if (start >= L) return;                 // uniform over the workgroup
-  const int kbeg = (int)start;
+  const int nact = (L + chunk - 1) / chunk;    // splits with keys
+  if (s >= nact) return;        // uniform over the workgroup (also L == 0)
+  const int kbeg = s * chunk;
   const int kend = min(L, kbeg + chunk);
   const __bf16* Kp = Kc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
   const __bf16* Vp = Vc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
@@ -103,8 +245,13 @@ __global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
                                                          8 * g4)
                       : bf16x8{};
 
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[kDecodeWaves][D * VSTR];
-  __bf16* vt = Vt[w];
+  // Per-wave LDS buffer of one V block; after the key loop the same memory
+  // holds the cross-wave merge.
+  constexpr int VBYTES = kDecodeWaves * kDecodeBlock * D * 2;
+  constexpr int MBYTES = kDecodeWaves * (32 + G * D) * 4;
+  static_assert(MBYTES <= VBYTES, "merge fits in the V buffers");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[VBYTES];
+  __bf16* vbuf = reinterpret_cast<__bf16*>(lds) + w * kDecodeBlock * D;
 
   f32x4 oacc[NDB];
 #pragma unroll
@@ -112,146 +259,56 @@ __global__ __launch_bounds__(kDecodeThreads) void attn_decode_split_kernel(
   float m_ref = -INFINITY;   // reference max (log2 domain) of head c16
   float l_i = 0.f;           // lane-partial sum for head c16
 
+  // This wave's blocks start at kbeg + 32w and step by 128.  Each block's K
+  // (registers) and V (LDS) loads are issued together and waited for once:
+  // with 16 resident waves per CU every wave has one block in flight.
+  DecodeK<D> blk;
   for (int j0 = kbeg + w * kDecodeBlock; j0 < kend;
        j0 += kDecodeWaves * kDecodeBlock) {
-    // --- loads: K as the A operand, V as coalesced rows (4 keys x 8 dims
-    // per lane and quad q).
-    bf16x8 ka[2][KT];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int key = j0 + 16 * kh + c16;
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-        ka[kh][t] = (key < kend) ? *reinterpret_cast<const bf16x8*>(
-                                       Kp + (size_t)key * D + 32 * t + 8 * g4)
-                                 : bf16x8{};
-    }
-    constexpr int VQ = kDecodeBlock / 16;     // key quads per lane
-    constexpr int VC = D / 8;                 // 16-byte chunks per row
-    static_assert(VC == 16 || VC == 8, "D = 128 or 64");
-    // lane -> (dim chunk, key quad): 16 lanes cover a 128-dim row; for D = 64
-    // the spare lanes take more quads.
-    constexpr int QPL = (kDecodeBlock / 4) / (64 / VC);   // quads per lane
-    u32x4 vr[QPL][4];
-#pragma unroll
-    for (int q = 0; q < QPL; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kq = lane / VC + (64 / VC) * q;
-        const int key = j0 + 4 * kq + i;
-        vr[q][i] = (key < kend) ? *reinterpret_cast<const u32x4*>(
-                                      Vp + (size_t)key * D + 8 * (lane % VC))
-                                : u32x4{};
-      }
-    (void)VQ;
-
-    // --- S^T = K Q^T
-    f32x4 sacc[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      sacc[kh] = f32x4{};
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
-        sacc[kh] = mfma_16x16x32_bf16(ka[kh][t], qB[t], sacc[kh]);
-    }
-    // lane holds head c16, keys j0 + 16kh + 4g4 + i
-    float x[8];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 16 * kh + 4 * g4 + i;
-        x[4 * kh + i] = (key < kend) ? sacc[kh][i] * scale_log2 : -INFINITY;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (mx > m_ref + kLazyRescale) {
-      // new reference (taken on the first block with a live key: m_ref is
-      // -inf there and the rescale factor is 0)
-      const float alpha = fast_exp2(m_ref - mx);
-      l_i *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-      m_ref = mx;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    bf16x8 pB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = fast_exp2(x[i] - m_use);
-      l_i += p;
-      pB[i] = (__bf16)p;
-    }
-
-    // --- V^T into this wave's LDS tile: dim e of keys 4kq..4kq+3 is one
-    // 8-byte run of row 8*(lane%VC) + e.
-#pragma unroll
-    for (int q = 0; q < QPL; ++q) {
-      const int kq = lane / VC + (64 / VC) * q;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1, sh = (e & 1) * 16;
-        u32x2 pr;
-        pr[0] = ((vr[q][0][wd] >> sh) & 0xffffu) |
-                (((vr[q][1][wd] >> sh) & 0xffffu) << 16);
-        pr[1] = ((vr[q][2][wd] >> sh) & 0xffffu) |
-                (((vr[q][3][wd] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&vt[(8 * (lane % VC) + e) * VSTR + 4 * kq]) =
-            pr;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // --- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const __bf16* row = &vt[(16 * db + c16) * VSTR + 4 * g4];
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[db] = mfma_16x16x32_bf16(a, pB, oacc[db]);
-    }
-    __builtin_amdgcn_wave_barrier();
+    decode_load<D>(blk, vbuf, Kp, Vp, j0, kend, lane);
+    decode_step<D>(blk, qB, vbuf, j0, kend, lane, scale_log2, m_ref, l_i,
+                   oacc);
   }
 
   // Per-wave state of head c16: m_ref, l (sum over the 4 lane groups),
   // O^T rows 16db + 4g4 + i.  Merge the waves through LDS.
   l_i += __shfl_xor(l_i, 16, 64);
   l_i += __shfl_xor(l_i, 32, 64);
-  __shared__ float sm_m[kDecodeWaves][16], sm_l[kDecodeWaves][16];
-  __shared__ float sm_o[kDecodeWaves][G][D];
+  __syncthreads();                       // every wave is done with its V
+  float* sm_m = reinterpret_cast<float*>(lds);            // [waves][16]
+  float* sm_l = sm_m + kDecodeWaves * 16;                 // [waves][16]
+  float* sm_o = sm_l + kDecodeWaves * 16;                 // [waves][G][D]
   if (g4 == 0) {
-    sm_m[w][c16] = m_ref;
-    sm_l[w][c16] = l_i;
+    sm_m[w * 16 + c16] = m_ref;
+    sm_l[w * 16 + c16] = l_i;
   }
   if (c16 < G) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][c16][16 * db + 4 * g4 + i] =
-          oacc[db][i];
+      for (int i = 0; i < 4; ++i)
+        sm_o[(w * G + c16) * D + 16 * db + 4 * g4 + i] = oacc[db][i];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kDecodeWaves; ++j) M = fmaxf(M, sm_m[j][h]);
+    for (int j = 0; j < kDecodeWaves; ++j) M = fmaxf(M, sm_m[j * 16 + h]);
     float W = 0.f, o = 0.f;
 #pragma unroll
     for (int j = 0; j < kDecodeWaves; ++j) {
-      const float wj = fast_exp2(sm_m[j][h] - M);   // 0 for an idle wave
-      W = fmaf(wj, sm_l[j][h], W);
-      o = fmaf(wj, sm_o[j][h][d], o);
+      const float wj = fast_exp2(sm_m[j * 16 + h] - M);  // 0 for an idle wave
+      W = fmaf(wj, sm_l[j * 16 + h], W);
+      o = fmaf(wj, sm_o[(j * G + h) * D + d], o);
     }
     const size_t row = ((size_t)(b * Hq + g * G + h)) * ns + s;
     ws_o[row * D + d] = o / W;
     if (d == 0) ws_lse[row] = (M + fast_log2(W)) * kLn2;
   }
+
 }
+
 
 // Combine the active splits of each (sequence, query head):
 // M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,

@@ -115,8 +115,10 @@ int attn_decode_auto_splits(int B, int Hkv);
  *   workspace: DEVICE scratch of at least
  *              attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) bytes,
  *              16-byte aligned, owned by the caller; its contents on entry
- *              do not matter and are overwritten.  Two calls in flight at
- *              once must not share a workspace.
+ *              do not matter and are overwritten.  Calls in flight at the
+ *              same time must not share a workspace.
+ * Two launches on `stream`: the split kernel writes each split's normalised
+ * partial output and LSE to the workspace, the combine kernel merges them.
  * Supported group sizes Hq / Hkv: 1, 2, 4, 8.
  */
 int attn_decode(const void* q, const void* kcache, const void* vcache,

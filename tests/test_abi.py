@@ -105,13 +105,24 @@ def test_decode_workspace_size():
     L = attn.lib()
     ns = attn.attn_decode_auto_splits(32, 2)
     assert 1 <= ns <= attn.MAX_SPLITS
-    rows = 32 * 8 * ns
-    want = (rows * 128 * 4 + 15) // 16 * 16 + rows * 4
-    assert L.attn_decode_workspace_size(32, 8, 2, 128, 0) == want
+
+    def want(B, Hq, Hkv, D, ns):
+        up = lambda x: (x + 15) // 16 * 16
+        rows = B * Hq * ns
+        return up(rows * D * 4) + up(rows * 4)
+    assert L.attn_decode_workspace_size(32, 8, 2, 128, 0) == \
+        want(32, 8, 2, 128, ns)
     assert L.attn_decode_workspace_size(32, 8, 2, 128, 5) == \
-        32 * 8 * 5 * 128 * 4 + 32 * 8 * 5 * 4
+        want(32, 8, 2, 128, 5)
+    assert L.attn_decode_workspace_size(3, 4, 1, 64, 7) == want(3, 4, 1, 64, 7)
     assert L.attn_decode_workspace_size(32, 8, 3, 128, 5) == 0
     assert L.attn_decode_workspace_size(32, 8, 2, 128, -1) == 0
+
+
+def test_auto_splits_depend_on_batch_only():
+    assert attn.attn_decode_auto_splits(32, 2) == 32
+    assert attn.attn_decode_auto_splits(1, 2) == attn.MAX_SPLITS
+    assert attn.attn_decode_auto_splits(1000, 8) == 32
 
 
 def test_binding_refuses_cpu_tensors():

@@ -238,6 +238,24 @@ def test_decode_equals_last_prefill_row():
     assert (lse - pl[:, :, L - 1]).abs().max() <= 1e-4
 
 
+def test_decode_workspace_reused_across_calls():
+    # one workspace serves many calls with different lengths
+    ws = attn.new_decode_workspace(4, 8, 2, 128, 7, DEV)
+    for seed, lens in enumerate([[100, 3000, 1, 640], [5, 5, 5, 5],
+                                 [4096, 0, 129, 2048]]):
+        sl, q, kc, vc = inputs.decode_inputs(4, 8, 2, 128, seqlens=lens,
+                                             seed=seed)
+        o, lse = attn.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV),
+                                  torch.from_numpy(sl).to(DEV), Hkv=2,
+                                  num_splits=7, with_lse=True, workspace=ws)
+        ro, rl = oracle.decode(np64(q), np64(kc), np64(vc), sl,
+                               1 / math.sqrt(128), 2)
+        live = np.asarray(sl) > 0
+        assert np.abs(np64(o)[live] - ro[live]).max() <= 2e-2
+        assert np.abs(lse.cpu().numpy()[live] - rl[live]).max() <= LSE_TOL
+    torch.cuda.synchronize()
+
+
 def test_decode_is_deterministic():
     sl, q, kc, vc = inputs.decode_inputs(8, 8, 2, 128, lmin=1, lmax=3000,
                                          seed=4)
