@@ -46,6 +46,50 @@ def decode_bytes(seqlens, Hq, Hkv, D, elt=2):
     return kv + 2 * len(seqlens) * Hq * D * elt
 
 
+KERNEL_SOURCES = ("causal_attention_amd/csrc/common.hpp",
+                  "causal_attention_amd/csrc/prefill.hpp",
+                  "causal_attention_amd/csrc/decode.hpp",
+                  "causal_attention_amd/csrc/attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    recorded in profiles/hbm_traffic.txt, or {} when that record was taken
+    on different kernel sources."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE)
+                  if ":" in line and not line.startswith("#"))
+    except OSError:
+        return {}
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_sources_sha256") != kernel_source_hash():
+        return {}
+    return kv
+
+
+def copy_calibration(mbytes, reps=5):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    import torch
+    n = int(mbytes * 1e6) // 16 * 16
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n,
+                      "reps": reps}), flush=True)
+
+
 def cpu_baseline(wp, wd):
     """Time the fp64 oracle on the host: the whole prefill workload once and
     the whole decode workload once."""
@@ -102,7 +146,13 @@ def main():
     ap.add_argument("--decode", default="c4_decode_b32")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    metavar="MB", help="only run a plain MB-sized device copy "
+                    "(to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): this "
@@ -175,6 +225,10 @@ def main():
     p_tflops = flops / (pf_avg * 1e-3) / 1e12
     d_gbs = dbytes / (dc_avg * 1e-3) / 1e9
 
+    tr = measured_traffic() if (wp.name, wd.name) == (
+        "c3_gqa_b4_s2048", "c4_decode_b32") else {}
+    p_traffic = int(tr["prefill_hbm_bytes_per_launch"]) if tr else None
+    d_traffic = int(tr["decode_hbm_bytes_per_launch"]) if tr else None
     out = {
         "metric": "prefill attention TFLOP/s + decode KV-cache GB/s, "
                   "% of MI355X roofline",
@@ -206,7 +260,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": p_traffic,
+            "traffic_unit": "HBM bytes per launch",
+            "algorithmic_bytes": prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.S,
+                                               wp.D),
             "flops_per_launch": flops,
             "avg_launch_us": round(pf_avg * 1e3, 3),
         },
@@ -222,7 +279,8 @@ def main():
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": round(d_gbs / PEAK_HBM_GBS, 4),
-                "traffic": None,
+                "traffic": d_traffic,
+                "traffic_unit": "HBM bytes per launch (split + combine)",
                 "bytes_per_launch": dbytes,
             },
         },
