@@ -22,11 +22,14 @@
 // argument (the scale must be positive).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace attn {
 
 constexpr int kPrefillThreads = 256;   // 4 waves
+
 constexpr int kPrefillBM = 128;        // query rows per workgroup
 
 // Block index -> (batch, KV head, query head, query tile).  Consecutive block
@@ -108,6 +111,18 @@ __device__ __forceinline__ void apply_mask(f32x16 (&x)[NKB], int j0, int hh,
       const bool dead = (key >= S) || (CAUSAL && key > query);
       x[kb][i] = dead ? -INFINITY : x[kb][i];
     }
+}
+
+// Causal / tail mask of one 32-key block (key base j0) of raw scores.
+template <bool CAUSAL>
+__device__ __forceinline__ void apply_mask_block(f32x16& x, int j0, int hh,
+                                                 int query, int S) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = j0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+    const bool dead = (key >= S) || (CAUSAL && key > query);
+    x[i] = dead ? -INFINITY : x[i];
+  }
 }
 
 // ---------------------------------------------------------------- bf16 path
@@ -214,67 +229,117 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     }
   };
 
-  auto compute_tile = [&](int j0, const __bf16* Kt, const __bf16* Vt) {
-    f32x16 sacc[NKB];
+  // One 64-key tile as two 32-key sub-blocks, each with its own row max and
+  // lazy-rescale check (the online softmax accepts any blocking), ordered so
+  // that independent MFMA and VALU work sit next to each other:
+  //   S0 = K0 Q^T;  [S1 = K1 Q^T  ||  P0 = exp2(S0)];  [O += V0^T P0  ||
+  //   P1 = exp2(S1)];  rescale O if S1 raised the max;  O += V1^T P1.
+  // P0 is accumulated with the reference it was computed against before
+  // any rescale for S1 is applied, so O, l and P stay consistent.
+  const int grp = lane >> 4, jl = lane & 15;
+  const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
+  const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
+  auto qk_sub = [&](const __bf16* Kt, int kb) {
+    f32x16 acc = f32x16{};
+    const int row = kb * 32 + r;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
-      const int row = kb * 32 + r;
+    for (int t = 0; t < KT; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          Kt + row * D + 8 * swz_k<CPR>(row, 2 * t + hh));
+      acc = mfma_32x32x16_bf16(a, qB[t], acc);
+    }
+    return acc;
+  };
+  auto pv_sub = [&](const __bf16* Vt, int kb, const bf16x8 (&pb)[2]) {
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Kt + row * D + 8 * swz_k<CPR>(row, 2 * t + hh));
-        sacc[kb] = mfma_32x32x16_bf16(a, qB[t], sacc[kb]);
+    for (int u = 0; u < 2; ++u) {
+      const int row0 = kb * 32 + 16 * u + vrow_off;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = db * 32 + vcol_off;
+        const int c = col >> 3, e = col & 7;
+        const bf16x4 lo = lds_read_tr16(Vt + row0 * D +
+                                        8 * swz_v<CPR>(row0, c) + e);
+        const bf16x4 hi = lds_read_tr16(Vt + (row0 + 8) * D +
+                                        8 * swz_v<CPR>(row0 + 8, c) + e);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3],
+                          hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = mfma_32x32x16_bf16(a, pb[u], oacc[db]);
       }
     }
-    // Only the diagonal and the ragged tail tiles need the elementwise mask
-    // (a wave-uniform, scalar branch).
-    if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
-      apply_mask<NKB, CAUSAL>(sacc, j0, hh, query, S);
-    softmax_step<NKB, NDB>(sacc, scale_log2, m_i, l_i, oacc);
-
-    // O^T += V^T P^T.  Lane group G = lane/16 reads dims 16*(G%2) of the
-    // 32-dim block and keys 4*(G/2) (+8) of the 16-key step, matching the
-    // key order of P^T in the B operand.
-    const int grp = lane >> 4, j = lane & 15;
-    const int vrow_off = 4 * (grp >> 1) + (j >> 2);
-    const int vcol_off = 16 * (grp & 1) + 4 * (j & 3);
+  };
+  // p = exp2(s*c + neg_m) as two bf16x8 B operands; returns the lane sum.
+  auto exp_sub = [&](const f32x16& sv, float neg_m, bf16x8 (&pb)[2]) {
+    float sum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pb;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) pb[s] = (__bf16)sacc[kb][8 * u + s];
-        const int row0 = kb * 32 + 16 * u + vrow_off;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int col = db * 32 + vcol_off;
-          const int c = col >> 3, e = col & 7;
-          const bf16x4 lo = lds_read_tr16(Vt + row0 * D +
-                                          8 * swz_v<CPR>(row0, c) + e);
-          const bf16x4 hi = lds_read_tr16(Vt + (row0 + 8) * D +
-                                          8 * swz_v<CPR>(row0 + 8, c) + e);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3],
-                            hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = mfma_32x32x16_bf16(a, pb, oacc[db]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(fmaf(sv[8 * u + i], scale_log2, neg_m));
+        sum += p;
+        pb[u][i] = (__bf16)p;
       }
+    return sum;
+  };
+  auto rowmax = [&](const f32x16& sv) {
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+    return fmaxf(mx, swap_halves(mx)) * scale_log2;
+  };
+  auto rescale = [&](float m_new) {
+    const float alpha = fast_exp2(m_i - m_new);
+    l_i *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    m_i = m_new;
   };
 
-  // Tile jt lives in buffer jt & 1.  Every wave computes every tile of the
-  // workgroup's range: a wave whose rows all lie above a tile's first keys
-  // gets p = 0 from the mask (skipping it with a branch would make the
-  // compiler copy the accumulator registers on every tile).
-  if (n_kv > 0) issue_tile(0, smem, smem + TILE);
-  for (int jt = 0; jt < n_kv; ++jt) {
+  auto tile_body = [&](auto mask_tag, int j0, const __bf16* Kt,
+                       const __bf16* Vt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0 = qk_sub(Kt, 0);
+    if constexpr (MASK) apply_mask_block<CAUSAL>(s0, j0, hh, query, S);
+    const float mx0 = rowmax(s0);
+    if (mx0 > m_i + kLazyRescale) rescale(mx0);
+    // A row with no visible key yet keeps m = -inf and gets p = 0.
+    const float neg_m0 = (m_i == -INFINITY) ? 0.f : -m_i;
+
+    f32x16 s1 = qk_sub(Kt, 1);
+    bf16x8 pb0[2];
+    l_i += exp_sub(s0, neg_m0, pb0);
+
+    if constexpr (MASK)
+      apply_mask_block<CAUSAL>(s1, j0 + 32, hh, query, S);
+    const float mx1 = rowmax(s1);
+    const bool up = mx1 > m_i + kLazyRescale;
+    const float m1 = up ? mx1 : m_i;
+    const float neg_m1 = (m1 == -INFINITY) ? 0.f : -m1;
+
+    pv_sub(Vt, 0, pb0);
+    bf16x8 pb1[2];
+    const float sum1 = exp_sub(s1, neg_m1, pb1);
+    if (up) rescale(mx1);
+    l_i += sum1;
+    pv_sub(Vt, 1, pb1);
+  };
+  // Tile jt lives in buffer jt & 1.  The leading tiles need no mask for any
+  // row of the workgroup; the rest (the causal diagonal and a ragged tail,
+  // at most three tiles) run a second loop with the elementwise mask.  Every
+  // wave computes every tile of the range: a wave whose rows all lie above
+  // a tile's keys gets p = 0 from the mask.
+  const int n_full = min(min(n_kv, S / BN), CAUSAL ? (q_lo + 1) / BN : n_kv);
+  auto step = [&](auto mask_tag, int jt) {
     wait_vmem();                  // this wave's loads of tile jt landed
     __syncthreads();              // everyone's landed; tile jt-1 consumed
     __bf16* cur = smem + (jt & 1) * 2 * TILE;
     __bf16* nxt = smem + ((jt + 1) & 1) * 2 * TILE;
     if (jt + 1 < n_kv) issue_tile(jt + 1, nxt, nxt + TILE);
-    compute_tile(jt * BN, cur, cur + TILE);
-  }
+    tile_body(mask_tag, jt * BN, cur, cur + TILE);
+  };
+  if (n_kv > 0) issue_tile(0, smem, smem + TILE);
+  for (int jt = 0; jt < n_full; ++jt) step(std::false_type{}, jt);
+  for (int jt = n_full; jt < n_kv; ++jt) step(std::true_type{}, jt);
 
   // Epilogue: O = acc / l (bf16, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
