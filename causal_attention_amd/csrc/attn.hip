@@ -15,6 +15,22 @@ using attn::kDecodeThreads;
 using attn::kPrefillBM;
 using attn::kPrefillThreads;
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).  Only used to order prefill blocks.
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
@@ -51,20 +67,21 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   const dim3 block(kPrefillThreads);
   const float sl2 = scale * attn::kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ncu = device_cu_count();
   if (D == 64) {
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
-                              sl2, n_qtiles);
+                              sl2, n_qtiles, ncu);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles);
+                               S, sl2, n_qtiles, ncu);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles);
+                               S, sl2, n_qtiles, ncu);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                                S, sl2, n_qtiles);
+                                S, sl2, n_qtiles, ncu);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -73,9 +90,9 @@ template <int D, bool C>
 struct Bf16Prefill {
   static void run(dim3 g, dim3 b, hipStream_t st, const __bf16* q,
                   const __bf16* k, const __bf16* v, __bf16* o, float* lse,
-                  int B, int Hq, int Hkv, int S, float sl2, int nq) {
+                  int B, int Hq, int Hkv, int S, float sl2, int nq, int ncu) {
     hipLaunchKernelGGL((attn::attn_prefill_bf16_kernel<D, C>), g, b, 0, st, q,
-                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq);
+                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
 };
 
@@ -83,9 +100,9 @@ template <int D, bool C>
 struct F32Prefill {
   static void run(dim3 g, dim3 b, hipStream_t st, const float* q,
                   const float* k, const float* v, float* o, float* lse, int B,
-                  int Hq, int Hkv, int S, float sl2, int nq) {
+                  int Hq, int Hkv, int S, float sl2, int nq, int ncu) {
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
-                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq);
+                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
 };
 

@@ -32,22 +32,37 @@ constexpr int kPrefillThreads = 256;   // 4 waves
 
 constexpr int kPrefillBM = 128;        // query rows per workgroup
 
-// Block index -> (batch, KV head, query head, query tile).  Consecutive block
-// indices walk over (batch, KV head) pairs first so that, when the pair count
-// is a multiple of 8, every block of one pair lands on the same XCD (blocks
-// are dealt to the 8 XCDs round-robin) and its K/V stay in that XCD's L2.
-// Query tiles are issued heaviest first (most key tiles under the causal
-// mask) so the short diagonal tiles fill the tail of the launch.
+// Block index -> (batch, KV head, query head, query tile).
+//
+// Work order: query tiles heaviest first (most key tiles under the causal
+// mask), so short tiles fill the tail of the launch.  Blocks are dealt to
+// the GPU in "rounds" of one block per CU (n_cu blocks); rounds with an odd
+// index are reversed (in groups of 8, see below), so the two blocks that
+// share a CU in the first wave of the launch are a heavy and a light one and
+// every CU starts with about the same total work ("snake" order).
+//
+// XCD locality: consecutive work indices walk over (batch, KV head) pairs
+// first, and blocks are dealt to the 8 XCDs round-robin, so when the pair
+// count is a multiple of 8 every block of one pair lands on the same XCD
+// and its K/V stay in that XCD's L2.  Reversing a round by whole groups of
+// 8 block indices keeps each block on the XCD of its pair.
 struct TileCoord {
   int b, g, hq, qt;
 };
 
-__device__ __forceinline__ TileCoord tile_coord(int bid, int B, int Hq,
-                                                int Hkv, int n_qtiles) {
+__device__ __forceinline__ TileCoord tile_coord(int bid, int nblocks, int B,
+                                                int Hq, int Hkv, int n_qtiles,
+                                                int n_cu) {
+  int idx = bid;
+  const int round = bid / n_cu;
+  if ((round & 1) && (round + 1) * n_cu <= nblocks && (n_cu & 7) == 0) {
+    const int pos = bid - round * n_cu;
+    idx = round * n_cu + (n_cu / 8 - 1 - pos / 8) * 8 + (pos & 7);
+  }
   const int G = Hq / Hkv;
   const int P = B * Hkv;
-  const int pair = bid % P;
-  const int rest = bid / P;
+  const int pair = idx % P;
+  const int rest = idx / P;
   TileCoord c;
   c.b = pair / Hkv;
   c.g = pair % Hkv;
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
-    int n_qtiles) {
+    int n_qtiles, int n_cu) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -186,7 +201,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   // wave index as a uniform (scalar) value, so per-wave branches are scalar
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const TileCoord tc = tile_coord(blockIdx.x, B, Hq, Hkv, n_qtiles);
+  const TileCoord tc =
+      tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
   const __bf16* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
   const __bf16* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
   const __bf16* Vp = V + (size_t)(tc.b * Hkv + tc.g) * S * D;
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
-    int n_qtiles) {
+    int n_qtiles, int n_cu) {
   constexpr int BM = kPrefillBM, BN = 32, NKB = BN / 32, NDB = D / 32;
   constexpr int HD = D / 2;                   // contraction elems per half
   constexpr int STR = D + 4;                  // LDS row stride (floats)
@@ -390,7 +406,8 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const TileCoord tc = tile_coord(blockIdx.x, B, Hq, Hkv, n_qtiles);
+  const TileCoord tc =
+      tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
   const float* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
   const float* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
   const float* Vp = V + (size_t)(tc.b * Hkv + tc.g) * S * D;
