@@ -22,7 +22,7 @@ STATUS = {
     -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_SPLITS", -8: "ATTN_ERR_LAUNCH",
     -9: "ATTN_ERR_SCALE",
 }
-MAX_SPLITS = 256
+MAX_SPLITS = 4096
 
 
 class AttnError(ValueError):

@@ -16,7 +16,7 @@ using attn::kPrefillBM;
 using attn::kPrefillThreads;
 
 // Compute units of the current device (cached per device; 256 if the query
-// fails).  Only used to order prefill blocks.
+// fails).  Orders prefill blocks and sizes the decode split.
 int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -108,17 +108,13 @@ struct F32Prefill {
 
 // ------------------------------------------------------------------ decode
 
+// Default number of key-block ranges for decode: two per compute unit (each
+// range is one single-wave workgroup).
 int auto_splits(int B, int Hkv) {
-  // Splits are at least 128 keys (one 32-key block per wave of a 4-wave
-  // workgroup).  Allow enough of them that short batches still fill the
-  // GPU (about 2048 workgroups), and at least 32 so caches up to 4096 keys
-  // are cut into 128-key chunks.
-  const long long pairs = (long long)B * Hkv;
-  if (pairs <= 0) return 32;
-  long long ns = (2048 + pairs - 1) / pairs;
-  if (ns < 32) ns = 32;
-  if (ns > ATTN_MAX_SPLITS) ns = ATTN_MAX_SPLITS;
-  return (int)ns;
+  (void)B;
+  (void)Hkv;
+  const int n = 2 * device_cu_count();
+  return n < ATTN_MAX_SPLITS ? n : ATTN_MAX_SPLITS;
 }
 
 int check_decode_sizes(int B, int Hq, int Hkv, int D, int num_splits) {
@@ -128,55 +124,58 @@ int check_decode_sizes(int B, int Hq, int Hkv, int D, int num_splits) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_ERR_GQA;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
-  if ((long long)B * Hkv > 65535LL * 65535LL || B > 65535 || Hkv > 65535)
-    return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
-// Workspace layout: fp32 partial outputs [B, Hq, ns, D], then fp32 partial
-// LSEs [B, Hq, ns], each starting on a 16-byte boundary.
+// Workspace layout: P + B*Hkv partial slots of G heads each (slot i + j holds
+// range i's piece of segment j = b*Hkv + g): fp32 outputs [slots, G, D], fp32
+// LSEs [slots, G], the ranges holding each segment's pieces [B*Hkv] (int2),
+// and the block total (int64), each part starting on a 16-byte boundary.
 struct DecodeWorkspace {
-  size_t o_off, lse_off, bytes;
+  size_t o_off, lse_off, seg_off, total_off, bytes;
 };
 
-DecodeWorkspace decode_workspace(int B, int Hq, int D, int ns) {
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int P) {
   auto up16 = [](size_t x) { return (x + 15) / 16 * 16; };
-  const size_t rows = (size_t)B * Hq * ns;
+  const size_t rows = ((size_t)P + (size_t)B * Hkv) * (size_t)(Hq / Hkv);
   DecodeWorkspace w;
   w.o_off = 0;
   w.lse_off = up16(rows * D * sizeof(float));
-  w.bytes = w.lse_off + up16(rows * sizeof(float));
+  w.seg_off = w.lse_off + up16(rows * sizeof(float));
+  w.total_off = w.seg_off + up16((size_t)B * Hkv * sizeof(int2));
+  w.bytes = w.total_off + 16;
   return w;
 }
 
 template <int D, int G>
 void launch_decode_dg(const __bf16* q, const __bf16* kc, const __bf16* vc,
                       const int* seqlens, __bf16* o, float* lse, float* ws_o,
-                      float* ws_lse, int B, int Hkv, int ns, float sl2,
-                      hipStream_t st) {
-  const dim3 grid(ns, Hkv, B);
-  hipLaunchKernelGGL((attn::attn_decode_split_kernel<D, G>), grid,
-                     dim3(kDecodeThreads), 0, st, q, kc, vc, seqlens, ws_o,
-                     ws_lse, Hkv, ns, sl2);
-  hipLaunchKernelGGL((attn::attn_decode_combine_kernel<D>),
-                     dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, seqlens,
-                     o, lse, Hkv * G, ns);
+                      float* ws_lse, int2* ws_seg, long long* ws_total, int B,
+                      int Hkv, int P, float sl2, hipStream_t st) {
+  hipLaunchKernelGGL((attn::attn_decode_split_kernel<D, G>), dim3(P), dim3(64),
+                     0, st, q, kc, vc, seqlens, o, lse, ws_o, ws_lse, ws_seg,
+                     ws_total, B, Hkv, P, sl2);
+  hipLaunchKernelGGL((attn::attn_decode_combine_kernel<D, G>),
+                     dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, ws_seg,
+                     ws_total, o, lse, Hkv, P);
 }
 
 template <int D>
 void launch_decode_d(int G, const __bf16* q, const __bf16* kc,
                      const __bf16* vc, const int* seqlens, __bf16* o,
-                     float* lse, float* ws_o, float* ws_lse, int B, int Hkv,
-                     int ns, float sl2, hipStream_t st) {
+                     float* lse, float* ws_o, float* ws_lse, int2* ws_seg,
+                     long long* ws_total, int B, int Hkv, int P, float sl2,
+                     hipStream_t st) {
   switch (G) {
     case 1: launch_decode_dg<D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   B, Hkv, ns, sl2, st); break;
+                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
     case 2: launch_decode_dg<D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   B, Hkv, ns, sl2, st); break;
+                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
     case 4: launch_decode_dg<D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   B, Hkv, ns, sl2, st); break;
+                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
     default: launch_decode_dg<D, 8>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                    B, Hkv, ns, sl2, st); break;
+                                    ws_seg, ws_total, B, Hkv, P, sl2, st); break;
   }
 }
 
@@ -213,8 +212,8 @@ int attn_decode_auto_splits(int B, int Hkv) { return auto_splits(B, Hkv); }
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
                                   int num_splits) {
   if (check_decode_sizes(B, Hq, Hkv, D, num_splits) != ATTN_OK) return 0;
-  const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
-  return decode_workspace(B, Hq, D, ns).bytes;
+  const int P = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  return decode_workspace(B, Hq, Hkv, D, P).bytes;
 }
 
 int attn_decode(const void* q, const void* kcache, const void* vcache,
@@ -228,16 +227,18 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
   if (!q || !kcache || !vcache || !seqlens || !o || !workspace)
     return ATTN_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) ||
-      !aligned(o, 2) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
+      !aligned(o, 16) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
       !aligned(workspace, 16))
     return ATTN_ERR_ALIGN;
-  const int ns = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
-  const DecodeWorkspace wl = decode_workspace(B, Hq, D, ns);
+  const int P = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  const DecodeWorkspace wl = decode_workspace(B, Hq, Hkv, D, P);
   if (workspace_bytes < wl.bytes) return ATTN_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
   float* ws_o = reinterpret_cast<float*>(ws + wl.o_off);
   float* ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+  int2* ws_seg = reinterpret_cast<int2*>(ws + wl.seg_off);
+  long long* ws_total = reinterpret_cast<long long*>(ws + wl.total_off);
   const int G = Hq / Hkv;
   const float sl2 = scale * attn::kLog2e;
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -246,11 +247,11 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
   const __bf16* vb = static_cast<const __bf16*>(vcache);
   __bf16* ob = static_cast<__bf16*>(o);
   if (D == 64)
-    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B,
-                        Hkv, ns, sl2, hs);
+    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
+                        ws_seg, ws_total, B, Hkv, P, sl2, hs);
   else
-    launch_decode_d<128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse, B,
-                         Hkv, ns, sl2, hs);
+    launch_decode_d<128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
+                         ws_seg, ws_total, B, Hkv, P, sl2, hs);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

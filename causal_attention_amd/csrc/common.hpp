@@ -85,4 +85,39 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS operand reads issued as inline assembly, for loops that keep
+// direct-to-LDS loads in flight on purpose: the compiler treats LDS reads it
+// can see as possibly aliasing every such load and would wait for all of
+// them.  The caller waits with lds_wait_all() and then passes each result
+// through lds_tie(), which orders its uses after the wait.  Addresses are
+// LDS byte addresses; OFF is an immediate byte offset.
+template <int OFF = 0>
+__device__ __forceinline__ void lds_read_b128_async(u32x4& v, unsigned addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2"
+               : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+template <int OFF = 0>
+__device__ __forceinline__ void lds_read_tr16_async(u32x2& v, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+               : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_wait_all() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+template <typename T>
+__device__ __forceinline__ void lds_tie(T& v) {
+  asm volatile("" : "+v"(v));
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 }  // namespace attn

@@ -1,41 +1,42 @@
 // Decode kernels: one query row per sequence against its packed KV cache,
-// split over the cache length, then a log-sum-exp combine.
+// split over the keys of the whole batch, then a log-sum-exp combine of the
+// pieces of each (sequence, query head) that were split.
 //
 // Method ("Attention三算子融合实战：从Triton到CUDA的推理加速优化"): the decode
 // setting of section 1.3 (one query row, K and V as long as the history), the
-// key split of section 4.4 (large key chunks handled by separate blocks, each
-// running the online softmax of section 2.2, merged across blocks
-// afterwards), and the partial-buffer-plus-reduce-kernel pattern of
-// "手写Triton kernel重构Qwen3.5-0.8B" section 3.3 (a separate small reduce
-// kernel rather than atomics).  GQA (section 2.1 of that page): the G = Hq/Hkv
-// query heads of one KV head are handled by the same workgroup, so each K/V
-// byte is read from HBM once, not once per query head.
+// key split of section 4.4 (key chunks handled by separate blocks, each
+// running the online softmax of section 2.2, merged afterwards), and the
+// partial-buffer-plus-reduce-kernel pattern of "手写Triton kernel重构
+// Qwen3.5-0.8B" section 3.3 (a separate small reduce kernel rather than
+// atomics).  GQA (section 2.1 of that page): the G = Hq/Hkv query heads of
+// one KV head are handled together, so each K/V byte is read from HBM once,
+// not once per query head.
 //
 // gfx950 mapping.  The path is bound by HBM bandwidth (about 4 FLOP per
-// byte); the arithmetic is put on v_mfma_f32_16x16x32_bf16 only so that it
-// costs almost no issue slots next to the loads.  Each wave takes 32-key
-// blocks of its split and keeps the next block's loads in flight while it
-// multiplies the current one:
-//  * S^T = K Q^T: the A operand is read straight from the cache into VGPRs
-//    (lane l holds key l%16 of a 16-key half, 8 consecutive dims), Q^T is the
-//    B operand with the G heads as columns (the other columns are zero).  The
-//    accumulator leaves lane l with head l%16 and keys 4*(l/16)..+3 of each
-//    half.
-//  * Those probabilities are re-used as the B operand of O^T = V^T P^T (key
-//    slot s of lane group l/16 is key 4*(l/16)+s of half 0 for s < 4, of half
-//    1 otherwise), so P never leaves registers.  V goes global -> LDS with
-//    gfx950's direct loads into a per-wave double buffer, and the A operand
-//    V^T comes from transposed LDS reads (ds_read_b64_tr_b16).
-//  * The row max and sum are per head, over the 4 lane groups: two cross-lane
-//    exchanges per block.  The running output is rescaled only when the max
-//    grows by more than 2^8 (exact: the final division by l cancels any
-//    common reference value; the bound keeps p <= 256).
-// The waves of a workgroup merge their (m, l, O) through LDS at the end and
-// write the split's normalised output and natural-log LSE to the workspace;
-// a second small kernel merges the splits of each (sequence, head).  (Doing
-// that merge in the last split to finish would need device-scope fences,
-// which on this 8-XCD part write back and invalidate a whole L2 per
-// workgroup: far slower than one more launch.)
+// byte), so the design goal is a steady stream of large, contiguous loads on
+// every CU from the first microsecond to the last:
+//  * Work split ("stream-K"): the caches are cut into 32-key blocks and the
+//    blocks of all (sequence, KV head) segments, in that order, are divided
+//    into P equal contiguous ranges, one per workgroup (P = the CU count by
+//    default).  Every workgroup gets the same number of blocks whatever the
+//    length mix, and all of them start together.  A segment that lies wholly
+//    in one range is finished by its workgroup; a segment cut by range
+//    boundaries leaves one partial (normalised output and LSE) per piece for
+//    the combine kernel.
+//  * Inside a workgroup each wave takes every 4th block of the current
+//    segment and streams it through a private double-buffered LDS ring:
+//    K, V and the segment's G query rows arrive by gfx950's direct loads
+//    (global_load_lds_dwordx4, 1 KB contiguous per instruction), the next
+//    block's loads are issued before the current one is multiplied, and no
+//    barrier is needed until the segment ends.
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (the heads
+//    are MFMA columns, the other columns are zero): the A operand K comes from
+//    LDS rows, V^T from transposed LDS reads (ds_read_b64_tr_b16), and the
+//    probabilities stay in registers as the B operand of the second product.
+//    The running output is rescaled only when the row max grows by more than
+//    2^8 (exact: the final division by l cancels any common reference).
+//  * At a segment end the waves merge (m, l, O) through LDS (each wave's free
+//    ring buffer) and one pass writes the final output or the partial.
 #pragma once
 
 #include "common.hpp"
@@ -44,327 +45,505 @@ namespace attn {
 
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-constexpr int kDecodeBlock = 32;                          // keys per wave step
-constexpr int kDecodeMinChunk = kDecodeWaves * kDecodeBlock;
-
-// Keys of split s for a sequence of L keys: [s*chunk, min(L, (s+1)*chunk)),
-// chunk a multiple of 32 and at least one block per wave.
-__device__ __forceinline__ int decode_chunk(int L, int ns) {
-  int c = max((L + ns - 1) / ns, kDecodeMinChunk);
-  return (c + kDecodeBlock - 1) / kDecodeBlock * kDecodeBlock;
-}
+constexpr int kDecodeBlock = 32;                  // keys per block
 
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b,
                                                     f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Wave-wide sum of a 64-bit value.
-__device__ __forceinline__ long long wave_sum64(long long x) {
+// T blocks cut into P equal contiguous ranges: range i starts at
+// floor(i*T/P) = q*i + floor(r*i/P) with T = q*P + r (r*i < P*P, so the
+// second division is 32-bit).
+struct Ranges {
+  long long q;
+  int r, P;
+  __device__ __forceinline__ Ranges(long long T, int P_) : P(P_) {
+    q = T / P_;
+    r = (int)(T - q * P_);
+  }
+  __device__ __forceinline__ long long lo(int i) const {
+    return q * i + (unsigned)(r * i) / (unsigned)P;
+  }
+  // The range holding block x (0 <= x < T): the largest i with lo(i) <= x.
+  __device__ __forceinline__ int owner(long long x) const {
+    int a = 0, b = P - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (lo(mid) <= x) a = mid; else b = mid - 1;
+    }
+    return a;
+  }
+};
+
+// Lane l's value of v as a wave-uniform (scalar) value.
+__device__ __forceinline__ long long lane_i64(long long v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffLL), l);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return ((long long)hi << 32) | (unsigned)lo;
+}
+
+// 64 consecutive sequences [base, base+64), one per lane: L (clamped to
+// >= 0), its 32-key block count, and the exclusive prefix sums of keys and of
+// blocks over all sequences before it.  kend / bend: the inclusive totals at
+// the end of the chunk (wave-uniform).
+struct SeqChunk {
+  int base;
+  int L, nb;
+  long long kx, bx;
+  long long kend, bend;
+};
+
+__device__ __forceinline__ SeqChunk load_chunk(const int* __restrict__ seqlens,
+                                               int B, int base, long long k0,
+                                               long long b0, int lane) {
+  SeqChunk c;
+  c.base = base;
+  const int b = base + lane;
+  c.L = (b < B) ? max(seqlens[b], 0) : 0;
+  c.nb = (c.L + kDecodeBlock - 1) / kDecodeBlock;
+  long long ki = c.L, bi = c.nb;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long kt = __shfl_up(ki, off, 64);
+    const long long bt = __shfl_up(bi, off, 64);
+    if (lane >= off) {
+      ki += kt;
+      bi += bt;
+    }
+  }
+  c.kx = k0 + ki - c.L;
+  c.bx = b0 + bi - c.nb;
+  c.kend = k0 + lane_i64(ki, 63);
+  c.bend = b0 + lane_i64(bi, 63);
+  return c;
 }
 
-// Direct global -> LDS load of 16 bytes per lane (lane order in LDS) and
-// the transposed LDS read (in each group of 16 lanes, lane j points at 4
-// dims of key row j/4; lane i receives dim i of those 4 keys).
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void dec_lds_load16(const void* g, __bf16* l) {
-  __builtin_amdgcn_global_load_lds(
-      g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
-}
-__device__ __forceinline__ bf16x4 dec_lds_read_tr16(const __bf16* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+// Total number of 32-key blocks over all sequences (one KV head).
+__device__ __forceinline__ long long total_blocks(const int* seqlens, int B,
+                                                  int lane) {
+  long long k0 = 0, b0 = 0;
+  for (int base = 0; base < B; base += 64) {
+    const SeqChunk c = load_chunk(seqlens, B, base, k0, b0, lane);
+    k0 = c.kend;
+    b0 = c.bend;
+  }
+  return b0;
 }
 
-// V block rows in LDS: 16-byte chunk c of key row r is stored at chunk
-// position c ^ f(r), so the 16 rows read by one transposed load hit distinct
-// banks (f is even, which keeps chunk pairs together).
+// One (sequence b, KV head g) segment, as a range [s0, s0 + nb) in the global
+// block order (segment-major: b*Hkv + g), with key offset kx of sequence b
+// and the part [a, e) of it that this workgroup processes.  Wave-uniform.
+struct DecodeSeg {
+  int b, g, L, nb;
+  long long kx, s0, a, e;
+  bool valid;
+};
+
+__device__ __forceinline__ DecodeSeg make_seg(const SeqChunk& c, int lane_b,
+                                              int g, int Hkv, long long lo,
+                                              long long hi) {
+  DecodeSeg s;
+  s.b = c.base + lane_b;
+  s.g = g;
+  s.L = __builtin_amdgcn_readlane(c.L, lane_b);
+  s.nb = __builtin_amdgcn_readlane(c.nb, lane_b);
+  s.kx = lane_i64(c.kx, lane_b);
+  s.s0 = lane_i64(c.bx, lane_b) * Hkv + (long long)g * s.nb;
+  s.a = max(lo, s.s0);
+  s.e = min(hi, s.s0 + s.nb);
+  s.valid = s.a < s.e;
+  return s;
+}
+
+// K rows in LDS: 16-byte chunk c of row r at chunk position c ^ f(r), so the
+// 16 rows read by one A-operand load hit distinct banks.
 template <int D>
-__device__ __forceinline__ int dec_swz(int row, int c) {
+__device__ __forceinline__ int dec_swz_k(int row, int c) {
+  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+}
+// V rows: the 16 rows of one transposed load hit distinct banks (f is even,
+// which keeps the chunk pairs of a transposed read together).
+template <int D>
+__device__ __forceinline__ int dec_swz_v(int row, int c) {
   return D == 128 ? (c ^ ((row & 7) << 1)) : (c ^ (((row >> 1) & 3) << 1));
 }
 
-// One 32-key block of one wave: K in registers as two 16-key MFMA A
-// operands; V goes straight to the wave's LDS buffer.
-template <int D>
-struct DecodeK {
-  bf16x8 ka[2][D / 32];
-};
-
-// Issue the loads of the block at key j0 (keys >= kend: K reads as zero,
-// V rows clamp to the last live key and are multiplied by p = 0).
-template <int D>
-__device__ __forceinline__ void decode_load(DecodeK<D>& blk, __bf16* vdst,
-                                            const __bf16* Kp,
-                                            const __bf16* Vp, int j0,
-                                            int kend, int lane) {
-  constexpr int KT = D / 32;
-  constexpr int CPR = D / 8;                 // chunks per row
-  constexpr int RPI = 64 / CPR;              // rows per load instruction
-  const int c16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const int key = j0 + 16 * kh + c16;
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-      blk.ka[kh][t] = (key < kend) ? *reinterpret_cast<const bf16x8*>(
-                                         Kp + (size_t)key * D + 32 * t + 8 * g4)
-                                   : bf16x8{};
-  }
-#pragma unroll
-  for (int i = 0; i < kDecodeBlock / RPI; ++i) {
-    const int row = i * RPI + lane / CPR, pos = lane % CPR;
-    const int key = min(j0 + row, kend - 1);
-    dec_lds_load16(Vp + (size_t)key * D + 8 * dec_swz<D>(row, pos),
-                   vdst + i * RPI * D);
-  }
-}
-
-// s_waitcnt vmcnt(N): at most N vector-memory loads of this wave in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Online-softmax step of one wave over one 32-key block whose V rows are in
-// vsrc (its loads are the only ones this wave has in flight).
-template <int D>
-__device__ __forceinline__ void decode_step(const DecodeK<D>& blk,
-                                            const bf16x8 (&qB)[D / 32],
-                                            const __bf16* vsrc, int j0,
-                                            int kend, int lane, float c,
-                                            float& m_ref, float& l_i,
-                                            f32x4 (&oacc)[D / 16]) {
-  constexpr int KT = D / 32;
-  constexpr int NDB = D / 16;
-  const int c16 = lane & 15, g4 = lane >> 4;
-
-  f32x4 sacc[2];
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    sacc[kh] = f32x4{};
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-      sacc[kh] = mfma_16x16x32_bf16(blk.ka[kh][t], qB[t], sacc[kh]);
-  }
-  // lane holds head c16, keys j0 + 16kh + 4g4 + i (raw q.k; masked = -inf)
-  float x[8];
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = j0 + 16 * kh + 4 * g4 + i;
-      x[4 * kh + i] = (key < kend) ? sacc[kh][i] : -INFINITY;
-    }
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-  if (mx > m_ref + kLazyRescale) {
-    // new reference (taken on the first block with a live key: m_ref is
-    // -inf there and the rescale factor is 0)
-    const float alpha = fast_exp2(m_ref - mx);
-    l_i *= alpha;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-    m_ref = mx;
-  }
-  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-  bf16x8 pB;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = fast_exp2(fmaf(x[i], c, neg_m));
-    l_i += p;
-    pB[i] = (__bf16)p;
-  }
-
-  wait_vmem_le<0>();               // this block's V rows have landed
-  // O^T += V^T P^T: lane group g4 reads keys 4g4..+3 and 16+4g4..+3 (the
-  // key order of P^T), dims 16db + (lane & 15).
-  const int r0 = 4 * g4 + (c16 >> 2);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int col = 16 * db + 4 * (c16 & 3);
-    const int ch = col >> 3, e = col & 7;
-    const bf16x4 lo = dec_lds_read_tr16(vsrc + r0 * D +
-                                        8 * dec_swz<D>(r0, ch) + e);
-    const bf16x4 hi = dec_lds_read_tr16(vsrc + (r0 + 16) * D +
-                                        8 * dec_swz<D>(r0 + 16, ch) + e);
-    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    oacc[db] = mfma_16x16x32_bf16(a, pB, oacc[db]);
-  }
+__device__ __forceinline__ void dec_lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(
+      g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads, 4) void attn_decode_split_kernel(
+struct DecodeLayout {
+  static constexpr int KT = D / 32;             // QK k-steps (32 dims)
+  static constexpr int NDB = D / 16;            // PV output blocks (16 dims)
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per load instruction
+  static constexpr int NKI = kDecodeBlock / RPI;     // instrs per K (or V)
+  static constexpr int QBYTES = (G * D * 2 + 1023) / 1024 * 1024;
+  static constexpr int NQI = QBYTES / 1024;          // instrs for Q
+  static constexpr int GROUP = 2 * NKI + NQI;        // instrs per block
+  static constexpr int KBYTES = kDecodeBlock * D * 2;
+  static constexpr int BUF = 2 * KBYTES + QBYTES;    // K | V | Q
+  static constexpr int LDS = 2 * BUF;                // double buffer
+};
+
+// One wave per workgroup, one key range per wave.
+template <int D, int G>
+__global__ __launch_bounds__(64) void attn_decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
     const __bf16* __restrict__ Vc, const int* __restrict__ seqlens,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hkv, int ns,
-    float scale_log2) {
-  constexpr int KT = D / 32;          // QK k-steps (32 dims each)
-  constexpr int NDB = D / 16;         // PV output blocks (16 dims each)
+    __bf16* __restrict__ O, float* __restrict__ LSE,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int2* __restrict__ ws_seg, long long* __restrict__ ws_total, int B,
+    int Hkv, int P, float scale_log2) {
+  using Lay = DecodeLayout<D, G>;
+  constexpr int KT = Lay::KT, NDB = Lay::NDB, CPR = Lay::CPR;
+  constexpr int RPI = Lay::RPI, NKI = Lay::NKI, NQI = Lay::NQI;
+  constexpr int BUF = Lay::BUF, KBYTES = Lay::KBYTES;
   static_assert(G <= 16, "heads are MFMA columns");
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[Lay::LDS];
+
+  const int lane = threadIdx.x;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int Hq = Hkv * G;
+  const int wg = blockIdx.x;
 
-  // L_b and the cache offset sum(L_0..L_{b-1}) from one load per lane.
-  long long prefix = 0;
-  int L = 0;
-  for (int base = 0; base <= b; base += 64) {
-    const int i = base + lane;
-    const int x = (i <= b) ? max(seqlens[i], 0) : 0;
-    if (b - base < 64) L = __shfl(x, b - base, 64);
-    prefix += wave_sum64(i < b ? x : 0);
-  }
-  const int chunk = decode_chunk(L, ns);
-  const int nact = (L + chunk - 1) / chunk;    // splits with keys
-  if (s >= nact) return;        // uniform over the workgroup (also L == 0)
-  const int kbeg = s * chunk;
-  const int kend = min(L, kbeg + chunk);
-  const __bf16* Kp = Kc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
-  const __bf16* Vp = Vc + ((size_t)prefix * Hkv + (size_t)g * L) * D;
+  // The key blocks of every (sequence, KV head) segment, in order, and this
+  // wave's range [lo, hi) of them.  For B <= 64 the first chunk of sequence
+  // lengths is kept for the search below.
+  SeqChunk ch = load_chunk(seqlens, B, 0, 0, 0, lane);
+  long long nblk = ch.bend;
+  for (int base = 64; base < B; base += 64)
+    nblk = load_chunk(seqlens, B, base, 0, nblk, lane).bend;
+  const long long T = nblk * Hkv;
+  const Ranges rg(T, P);
+  const long long lo = rg.lo(wg), hi = rg.lo(wg + 1);
 
-  // Q^T as the B operand: column c16 is head g*G + c16 (zero if c16 >= G),
-  // k-step t covers dims 32t + 8*g4 .. +7.
-  bf16x8 qB[KT];
-  const __bf16* qrow = Q + (size_t)(b * Hq + g * G + min(c16, G - 1)) * D;
-#pragma unroll
-  for (int t = 0; t < KT; ++t)
-    qB[t] = (c16 < G) ? *reinterpret_cast<const bf16x8*>(qrow + 32 * t +
-                                                         8 * g4)
-                      : bf16x8{};
-
-  // Per-wave LDS buffer of one V block; after the key loop the same memory
-  // holds the cross-wave merge.
-  constexpr int VBYTES = kDecodeWaves * kDecodeBlock * D * 2;
-  constexpr int MBYTES = kDecodeWaves * (32 + G * D) * 4;
-  static_assert(MBYTES <= VBYTES, "merge fits in the V buffers");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[VBYTES];
-  __bf16* vbuf = reinterpret_cast<__bf16*>(lds) + w * kDecodeBlock * D;
-
-  f32x4 oacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{};
-  float m_ref = -INFINITY;   // reference max (log2 domain) of head c16
-  float l_i = 0.f;           // lane-partial sum for head c16
-
-  // This wave's blocks start at kbeg + 32w and step by 128.  Each block's K
-  // (registers) and V (LDS) loads are issued together and waited for once:
-  // with 16 resident waves per CU every wave has one block in flight.
-  DecodeK<D> blk;
-  for (int j0 = kbeg + w * kDecodeBlock; j0 < kend;
-       j0 += kDecodeWaves * kDecodeBlock) {
-    decode_load<D>(blk, vbuf, Kp, Vp, j0, kend, lane);
-    decode_step<D>(blk, qB, vbuf, j0, kend, lane, scale_log2, m_ref, l_i,
-                   oacc);
-  }
-
-  // Per-wave state of head c16: m_ref, l (sum over the 4 lane groups),
-  // O^T rows 16db + 4g4 + i.  Merge the waves through LDS.
-  l_i += __shfl_xor(l_i, 16, 64);
-  l_i += __shfl_xor(l_i, 32, 64);
-  __syncthreads();                       // every wave is done with its V
-  float* sm_m = reinterpret_cast<float*>(lds);            // [waves][16]
-  float* sm_l = sm_m + kDecodeWaves * 16;                 // [waves][16]
-  float* sm_o = sm_l + kDecodeWaves * 16;                 // [waves][G][D]
-  if (g4 == 0) {
-    sm_m[w * 16 + c16] = m_ref;
-    sm_l[w * 16 + c16] = l_i;
-  }
-  if (c16 < G) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm_o[(w * G + c16) * D + 16 * db + 4 * g4 + i] = oacc[db][i];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kDecodeWaves; ++j) M = fmaxf(M, sm_m[j * 16 + h]);
-    float W = 0.f, o = 0.f;
-#pragma unroll
-    for (int j = 0; j < kDecodeWaves; ++j) {
-      const float wj = fast_exp2(sm_m[j * 16 + h] - M);  // 0 for an idle wave
-      W = fmaf(wj, sm_l[j * 16 + h], W);
-      o = fmaf(wj, sm_o[(j * G + h) * D + d], o);
+  // Workgroup 0: the block total for the combine kernel, and sequences
+  // without keys (o = 0, lse = -inf, nothing to combine).
+  if (wg == 0) {
+    if (lane == 0) *ws_total = T;
+    for (int base = 0; base < B; base += 64) {
+      const int b = base + lane;
+      if (b < B && seqlens[b] <= 0) {
+        for (int i = 0; i < Hq * D; i += 8)
+          *reinterpret_cast<u32x4*>(O + (size_t)b * Hq * D + i) = u32x4{};
+        if (LSE != nullptr)
+          for (int h = 0; h < Hq; ++h) LSE[(size_t)b * Hq + h] = -INFINITY;
+        for (int g = 0; g < Hkv; ++g) ws_seg[(size_t)b * Hkv + g] = int2{1, 0};
+      }
     }
-    const size_t row = ((size_t)(b * Hq + g * G + h)) * ns + s;
-    ws_o[row * D + d] = o / W;
-    if (d == 0) ws_lse[row] = (M + fast_log2(W)) * kLn2;
   }
+  if (lo >= hi) return;
 
+  // The segment holding block lo.
+  int lb = 0, g0 = 0;
+  for (;;) {
+    const long long s = ch.bx * Hkv, e = (ch.bx + ch.nb) * Hkv;
+    const unsigned long long hit =
+        __ballot(ch.base + lane < B && s <= lo && lo < e);
+    if (hit) {
+      lb = __builtin_ctzll(hit);
+      const long long sb = lane_i64(ch.bx, lb) * Hkv;
+      const int nbb = __builtin_amdgcn_readlane(ch.nb, lb);
+      g0 = (int)((lo - sb) / nbb);
+      break;
+    }
+    ch = load_chunk(seqlens, B, ch.base + 64, ch.kend, ch.bend, lane);
+  }
+  DecodeSeg cur = make_seg(ch, lb, g0, Hkv, lo, hi);
+
+  // The segment after `s` (next KV head, else the next sequence with keys),
+  // or an invalid one when `s` reaches the end of the range.
+  auto next_seg = [&](const DecodeSeg& s) {
+    if (s.e >= hi) {
+      DecodeSeg n = s;
+      n.valid = false;
+      return n;
+    }
+    if (s.g + 1 < Hkv) return make_seg(ch, lb, s.g + 1, Hkv, lo, hi);
+    for (;;) {
+      const unsigned long long more =
+          __ballot(lane > lb && ch.base + lane < B && ch.nb > 0);
+      if (more) {
+        lb = __builtin_ctzll(more);
+        return make_seg(ch, lb, 0, Hkv, lo, hi);
+      }
+      // blocks remain in the range, so a later chunk holds them
+      ch = load_chunk(seqlens, B, ch.base + 64, ch.kend, ch.bend, lane);
+      lb = -1;
+    }
+  };
+
+  // Per-lane byte offsets of the direct loads: K / V row i*RPI + lane/CPR
+  // of a block with its chunks swizzled, and element lane*8 (+512 per
+  // instruction) of the query rows.
+  unsigned koff[NKI], voff[NKI], qoff[NQI];
+#pragma unroll
+  for (int i = 0; i < NKI; ++i) {
+    const int row = i * RPI + lane / CPR, pos = lane % CPR;
+    koff[i] = (row * D + 8 * dec_swz_k<D>(row, pos)) * 2;
+    voff[i] = (row * D + 8 * dec_swz_v<D>(row, pos)) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < NQI; ++i) qoff[i] = min((i * 64 + lane) * 8, G * D - 8) * 2;
+
+  // Direct loads of block blk of segment s into buffer buf: K and V rows
+  // (past the end of the sequence: row L-1, whose score is masked) and the
+  // segment's G query rows.
+  auto issue = [&](const DecodeSeg& s, long long blk, int buf) {
+    const int k0 = (int)(blk - s.s0) * kDecodeBlock;
+    const size_t seg_off = ((size_t)s.kx * Hkv + (size_t)s.g * s.L) * D;
+    const char* Kp = reinterpret_cast<const char*>(Kc + seg_off);
+    const char* Vp = reinterpret_cast<const char*>(Vc + seg_off);
+    unsigned char* kb = lds + buf * BUF;
+    if (k0 + kDecodeBlock <= s.L) {
+      const char* Kb = Kp + (size_t)k0 * D * 2;
+      const char* Vb = Vp + (size_t)k0 * D * 2;
+#pragma unroll
+      for (int i = 0; i < NKI; ++i) {
+        dec_lds_load16(Kb + koff[i], kb + i * 1024);
+        dec_lds_load16(Vb + voff[i], kb + KBYTES + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NKI; ++i) {
+        const int row = i * RPI + lane / CPR;
+        const int d = (min(k0 + row, s.L - 1) - (k0 + row)) * D * 2;
+        const char* Kb = Kp + (size_t)k0 * D * 2 + d;
+        const char* Vb = Vp + (size_t)k0 * D * 2 + d;
+        dec_lds_load16(Kb + koff[i], kb + i * 1024);
+        dec_lds_load16(Vb + voff[i], kb + KBYTES + i * 1024);
+      }
+    }
+    const char* Qp = reinterpret_cast<const char*>(
+        Q + ((size_t)s.b * Hq + (size_t)s.g * G) * D);
+#pragma unroll
+    for (int i = 0; i < NQI; ++i)
+      dec_lds_load16(Qp + qoff[i], kb + 2 * KBYTES + i * 1024);
+  };
+
+  // Online-softmax state of head c16: reference max (log2 domain),
+  // lane-partial sum, O^T rows 16db + 4g4 + i.
+  f32x4 oacc[NDB];
+  float m_ref = -INFINITY, l_i = 0.f;
+
+  const unsigned lds_base = lds_addr(lds);
+  // One block: keys k0 .. k0+31 of segment s, in buffer buf.
+  auto compute = [&](const DecodeSeg& s, long long blk, int buf) {
+    const unsigned kb = lds_base + buf * BUF;
+    const int k0 = (int)(blk - s.s0) * kDecodeBlock;
+    // Q^T (B operand): column c16 = head c16 (zero for c16 >= G), dims
+    // 32t + 8g4 .. +7.  K (A operand): rows 16kh + c16, same dims.
+    u32x4 qv[KT], kv[2][KT];
+    const int qh = min(c16, G - 1);
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      lds_read_b128_async(qv[t], kb + 2 * KBYTES + qh * D * 2 +
+                                     (32 * t + 8 * g4) * 2);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int row = 16 * kh + c16;
+        lds_read_b128_async(kv[kh][t],
+                            kb + row * D * 2 +
+                                16 * dec_swz_k<D>(row, 4 * t + g4));
+      }
+    // V^T (A operand): lane group g4 reads keys 4g4..+3 and 16+4g4..+3 (the
+    // key order of P^T), dims 16db + (lane & 15).
+    u32x2 vlo[NDB], vhi[NDB];
+    const int r0 = 4 * g4 + (c16 >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 16 * db + 4 * (c16 & 3);
+      const int cc = col >> 3, e = col & 7;
+      lds_read_tr16_async(vlo[db], kb + KBYTES + r0 * D * 2 +
+                                       16 * dec_swz_v<D>(r0, cc) + 2 * e);
+      lds_read_tr16_async(vhi[db], kb + KBYTES + (r0 + 16) * D * 2 +
+                                       16 * dec_swz_v<D>(r0 + 16, cc) + 2 * e);
+    }
+    lds_wait_all();
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      lds_tie(qv[t]);
+      lds_tie(kv[0][t]);
+      lds_tie(kv[1][t]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      lds_tie(vlo[db]);
+      lds_tie(vhi[db]);
+    }
+
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      sacc[kh] = f32x4{};
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const bf16x8 qb = (c16 < G) ? __builtin_bit_cast(bf16x8, qv[t])
+                                    : bf16x8{};
+        sacc[kh] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kh][t]),
+                                      qb, sacc[kh]);
+      }
+    }
+    // lane holds head c16, keys k0 + 16kh + 4g4 + i (raw q.k; masked = -inf)
+    float x[8];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 16 * kh + 4 * g4 + i;
+        x[4 * kh + i] = (key < s.L) ? sacc[kh][i] : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (mx > m_ref + kLazyRescale) {
+      // new reference (every block has a live key, so on a segment's first
+      // block m_ref is -inf, mx is finite and the rescale factor is 0)
+      const float alpha = fast_exp2(m_ref - mx);
+      l_i *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+      m_ref = mx;
+    }
+    const float neg_m = -m_ref;
+    bf16x8 pB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = fast_exp2(fmaf(x[i], scale_log2, neg_m));
+      l_i += p;
+      pB[i] = (__bf16)p;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x4 a = {vlo[db][0], vlo[db][1], vhi[db][0], vhi[db][1]};
+      oacc[db] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pB,
+                                    oacc[db]);
+    }
+  };
+
+  // This wave's blocks lo .. hi-1 in order; the next one is put in flight
+  // before the current one is multiplied, across segment ends too.
+  issue(cur, lo, 0);
+  int n = 0;                          // blocks multiplied so far
+  for (;;) {
+    const DecodeSeg nxt = next_seg(cur);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x4{};
+    m_ref = -INFINITY;
+    l_i = 0.f;
+    for (long long blk = cur.a; blk < cur.e; ++blk) {
+      if (blk + 1 < cur.e) {
+        issue(cur, blk + 1, (n + 1) & 1);
+        wait_vmem_le<Lay::GROUP>();
+      } else if (nxt.valid) {
+        issue(nxt, nxt.a, (n + 1) & 1);
+        wait_vmem_le<Lay::GROUP>();
+      } else {
+        wait_vmem_le<0>();
+      }
+      compute(cur, blk, n & 1);
+      ++n;
+    }
+    // Segment end: the final output when the whole segment is in this
+    // range, else this piece's normalised output and LSE.
+    l_i += __shfl_xor(l_i, 16, 64);
+    l_i += __shfl_xor(l_i, 32, 64);
+    if (c16 < G) {
+      const float inv = 1.f / l_i;
+      const float lse = (m_ref + fast_log2(l_i)) * kLn2;
+      if (cur.s0 >= lo && cur.s0 + cur.nb <= hi) {
+        const size_t row = (size_t)cur.b * Hq + (size_t)cur.g * G + c16;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          u32x2 pr;
+          pr[0] = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+          pr[1] = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+          *reinterpret_cast<u32x2*>(O + row * D + 16 * db + 4 * g4) = pr;
+        }
+        if (LSE != nullptr && g4 == 0) LSE[row] = lse;
+      } else {
+        const size_t row =
+            ((size_t)wg + (size_t)cur.b * Hkv + cur.g) * G + c16;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          *reinterpret_cast<f32x4*>(ws_o + row * D + 16 * db + 4 * g4) =
+              oacc[db] * inv;
+        if (g4 == 0) ws_lse[row] = lse;
+      }
+    }
+    // The range holding a segment's first block records which ranges hold
+    // its pieces (one range: finished here).
+    if (lane == 0 && cur.a == cur.s0)
+      ws_seg[(size_t)cur.b * Hkv + cur.g] =
+          int2{wg, rg.owner(cur.s0 + cur.nb - 1)};
+    if (!nxt.valid) break;
+    cur = nxt;
+  }
 }
 
-
-// Combine the active splits of each (sequence, query head):
-// M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
-// lse = M + ln(sum w_s).  A sequence with no keys gives o = 0, lse = -inf.
-// One workgroup of D threads per (sequence, head); the split weights are
-// formed once in LDS and the partial rows are read 8 at a time.
-template <int D>
+// Combine the pieces of each (sequence, KV head) segment that range
+// boundaries cut: M = max lse_i, w_i = exp(lse_i - M),
+// o = sum w_i o_i / sum w_i, lse = M + ln(sum w_i).  One workgroup of D
+// threads per (sequence, query head).  The split kernel recorded the ranges
+// holding the pieces; a segment finished in one range, or a sequence without
+// keys, needs nothing here.  Pieces are taken 16 at a time, with their LSEs
+// and partial rows all in flight together.
+template <int D, int G>
 __global__ __launch_bounds__(D) void attn_decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
-    const int* __restrict__ seqlens, __bf16* __restrict__ O,
-    float* __restrict__ LSE, int Hq, int ns) {
-  const int bh = blockIdx.x;
-  const int b = bh / Hq;
+    const int2* __restrict__ ws_seg, const long long* __restrict__ ws_total,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hkv, int P) {
+  constexpr int TB = 16;
+  __shared__ float s_m[TB];
+  const int j = blockIdx.x / G, h = blockIdx.x % G;
   const int d = threadIdx.x;
-  const int L = max(seqlens[b], 0);
-  const int chunk = decode_chunk(L, ns);
-  const int nact = (L + chunk - 1) / chunk;
-  const float* lse_p = ws_lse + (size_t)bh * ns;
-  const float* o_p = ws_o + (size_t)bh * ns * D;
+  const int Hq = Hkv * G;
+  const int2 sg = ws_seg[j];
+  if (sg.x >= sg.y) return;
+  const Ranges rg(*ws_total, P);
+  const size_t orow = (size_t)(j / Hkv) * Hq + (size_t)(j % Hkv) * G + h;
 
-  __shared__ float wgt[256];
-  __shared__ float red[D / 64];
-  float mloc = -INFINITY;
-  for (int s = d; s < nact; s += D) mloc = fmaxf(mloc, lse_p[s]);
+  float M = -INFINITY, W = 0.f, o = 0.f;
+  for (int c0 = sg.x; c0 <= sg.y; c0 += TB) {
+    const int n = min(TB, sg.y - c0 + 1);
+    // piece d's LSE (empty ranges hold no piece: -inf), and this thread's
+    // dimension of all n pieces, issued together
+    float lse_d = -INFINITY;
+    if (d < n && rg.lo(c0 + d) < rg.lo(c0 + d + 1))
+      lse_d = ws_lse[((size_t)(c0 + d) + j) * G + h];
+    float v[TB];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1)
-    mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-  if ((d & 63) == 0) red[d >> 6] = mloc;
-  __syncthreads();
-  float M = red[0];
+    for (int t = 0; t < TB; ++t)
+      v[t] = t < n ? ws_o[(((size_t)c0 + t + j) * G + h) * D + d] : 0.f;
+    __syncthreads();                   // previous round's s_w / s_m read
+    if (d < TB) s_m[d] = lse_d;
+    __syncthreads();
+    float mc = -INFINITY;
 #pragma unroll
-  for (int i = 1; i < D / 64; ++i) M = fmaxf(M, red[i]);
-  for (int s = d; s < nact; s += D)
-    wgt[s] = fast_exp2((lse_p[s] - M) * kLog2e);
-  __syncthreads();
-
-  float W = 0.f, o = 0.f;
-  int s = 0;
-  for (; s + 8 <= nact; s += 8) {
-    float v[8];
+    for (int t = 0; t < TB; ++t) mc = fmaxf(mc, s_m[t]);
+    const float Mn = fmaxf(M, mc);
+    const float a = fast_exp2((M - Mn) * kLog2e);       // 0 on first round
+    W *= a;
+    o *= a;
+    M = Mn;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = o_p[(size_t)(s + u) * D + d];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      W += wgt[s + u];
-      o = fmaf(wgt[s + u], v[u], o);
+    for (int t = 0; t < TB; ++t) {
+      const float w = fast_exp2((s_m[t] - Mn) * kLog2e);   // 0 when empty
+      W += w;
+      o = fmaf(w, w > 0.f ? v[t] : 0.f, o);
     }
   }
-  for (; s < nact; ++s) {
-    W += wgt[s];
-    o = fmaf(wgt[s], o_p[(size_t)s * D + d], o);
-  }
-  const float res = nact > 0 ? o / W : 0.f;
-  O[(size_t)bh * D + d] = (__bf16)res;
-  if (LSE != nullptr && d == 0)
-    LSE[bh] = nact > 0 ? M + logf(W) : -INFINITY;
+  O[orow * D + d] = (__bf16)(o / W);
+  if (LSE != nullptr && d == 0) LSE[orow] = M + logf(W);
 }
 
 }  // namespace attn

@@ -52,7 +52,7 @@ typedef enum {
 } attn_status;
 
 /* Largest num_splits attn_decode accepts. */
-#define ATTN_MAX_SPLITS 256
+#define ATTN_MAX_SPLITS 4096
 
 /*
  * Prefill attention, bf16 storage.
@@ -89,17 +89,18 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
                                   int num_splits);
 
-/* The split count attn_decode uses for num_splits == 0 (depends on B and
-   Hkv only: nothing is read back from the device). */
+/* The split count attn_decode uses for num_splits == 0: twice the number of
+   compute units of the current device (512 when it cannot be queried;
+   nothing is read back from the device, and B and Hkv do not change it). */
 int attn_decode_auto_splits(int B, int Hkv);
 
 /*
  * Decode attention: one query row per sequence against its whole KV cache
  * (the decode setting of the attention-fusion page, section 1.3: Q has one
- * row while K and V grow with the history), split over the cache length and
- * merged with a log-sum-exp combine (section 4.4: key chunks handled by
- * separate blocks and merged afterwards; section 2.2: the merge order does
- * not matter once m and l are kept).
+ * row while K and V grow with the history), split over the keys and merged
+ * with a log-sum-exp combine (section 4.4: key chunks handled by separate
+ * blocks and merged afterwards; section 2.2: the merge order does not matter
+ * once m and l are kept).
  *   q, o     : [B, Hq, D] bf16
  *   kcache,
  *   vcache   : packed per sequence: sequence b is a [Hkv, L_b, D] bf16 block
@@ -107,9 +108,11 @@ int attn_decode_auto_splits(int B, int Hkv);
  *   seqlens  : DEVICE int32 [B], L_b = number of cached keys the query of
  *              sequence b attends to (its own key included).  L_b <= 0 gives
  *              o = 0 and lse = -inf for that sequence.
- *   num_splits: key chunks per sequence, 1..ATTN_MAX_SPLITS, or 0 for
- *              attn_decode_auto_splits(B, Hkv).  A sequence is cut into at
- *              most num_splits chunks of at least 64 keys.
+ *   num_splits: 1..ATTN_MAX_SPLITS, or 0 for attn_decode_auto_splits(B, Hkv).
+ *              The caches are cut into 32-key blocks; the blocks of all
+ *              (sequence, KV head) pairs, in that order, are divided into
+ *              num_splits equal contiguous ranges, one per workgroup, so the
+ *              work per workgroup does not depend on the length mix.
  *   scale    : multiplier of q.k, finite and > 0.
  *   lse      : [B, Hq] fp32 natural-log LSE, or NULL.
  *   workspace: DEVICE scratch of at least
@@ -117,8 +120,11 @@ int attn_decode_auto_splits(int B, int Hkv);
  *              16-byte aligned, owned by the caller; its contents on entry
  *              do not matter and are overwritten.  Calls in flight at the
  *              same time must not share a workspace.
- * Two launches on `stream`: the split kernel writes each split's normalised
- * partial output and LSE to the workspace, the combine kernel merges them.
+ * Two launches on `stream`: the split kernel streams each range, finishes
+ * every (sequence, KV head) pair whose blocks all lie in one range, and for
+ * a pair cut by range boundaries writes one normalised partial output and
+ * LSE per piece (plus which ranges hold them) to the workspace; the combine
+ * kernel merges those pieces (log-sum-exp combine).
  * Supported group sizes Hq / Hkv: 1, 2, 4, 8.
  */
 int attn_decode(const void* q, const void* kcache, const void* vcache,

@@ -106,10 +106,12 @@ def test_decode_workspace_size():
     ns = attn.attn_decode_auto_splits(32, 2)
     assert 1 <= ns <= attn.MAX_SPLITS
 
-    def want(B, Hq, Hkv, D, ns):
+    # P + B*Hkv partial slots of G heads (outputs, then LSEs), the piece
+    # ranges of each (sequence, KV head) as int2, and the int64 block total
+    def want(B, Hq, Hkv, D, P):
         up = lambda x: (x + 15) // 16 * 16
-        rows = B * Hq * ns
-        return up(rows * D * 4) + up(rows * 4)
+        rows = (P + B * Hkv) * (Hq // Hkv)
+        return up(rows * D * 4) + up(rows * 4) + up(B * Hkv * 8) + 16
     assert L.attn_decode_workspace_size(32, 8, 2, 128, 0) == \
         want(32, 8, 2, 128, ns)
     assert L.attn_decode_workspace_size(32, 8, 2, 128, 5) == \
@@ -117,12 +119,20 @@ def test_decode_workspace_size():
     assert L.attn_decode_workspace_size(3, 4, 1, 64, 7) == want(3, 4, 1, 64, 7)
     assert L.attn_decode_workspace_size(32, 8, 3, 128, 5) == 0
     assert L.attn_decode_workspace_size(32, 8, 2, 128, -1) == 0
+    assert L.attn_decode_workspace_size(32, 8, 2, 128, attn.MAX_SPLITS) == \
+        want(32, 8, 2, 128, attn.MAX_SPLITS)
 
 
-def test_auto_splits_depend_on_batch_only():
-    assert attn.attn_decode_auto_splits(32, 2) == 32
-    assert attn.attn_decode_auto_splits(1, 2) == attn.MAX_SPLITS
-    assert attn.attn_decode_auto_splits(1000, 8) == 32
+def test_auto_splits_depend_on_the_device_only():
+    # two single-wave ranges per compute unit; without a GPU the library
+    # assumes 256 compute units
+    import torch
+    n = attn.attn_decode_auto_splits(32, 2)
+    assert n == attn.attn_decode_auto_splits(1, 2)
+    assert n == attn.attn_decode_auto_splits(1000, 8)
+    if not torch.cuda.is_available():
+        assert n == 512
+    assert n % 2 == 0 and 2 <= n <= attn.MAX_SPLITS
 
 
 def test_binding_refuses_cpu_tensors():

@@ -207,6 +207,37 @@ def test_decode_empty_sequences():
     check_decode([0, 10, 0, 300], 8, 2, 128, seed=5)
 
 
+@pytest.mark.parametrize("num_splits", [0, 37, 1000])
+def test_decode_many_sequences(num_splits):
+    # more than 64 sequences: the per-sequence lengths are scanned in chunks
+    # of 64, with empty sequences and a segment crossing chunk ends
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 400, size=150)
+    lens[[0, 63, 64, 65, 149]] = [0, 0, 2000, 0, 33]
+    check_decode(lens.tolist(), 8, 2, 128, num_splits=num_splits, seed=17)
+
+
+@pytest.mark.parametrize("num_splits", [512, attn.MAX_SPLITS])
+def test_decode_more_ranges_than_blocks(num_splits):
+    # 35 blocks per KV head, 70 in all: most ranges are empty, some of them
+    # between two pieces of one sequence
+    check_decode([40, 1000, 3], 8, 2, 128, num_splits=num_splits, seed=19)
+
+
+def test_decode_workspace_contents_do_not_matter():
+    sl, q, kc, vc = inputs.decode_inputs(3, 8, 2, 128, seqlens=[900, 0, 77],
+                                         seed=23)
+    args = (q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(sl).to(DEV))
+    ws = attn.new_decode_workspace(3, 8, 2, 128, 64, DEV)
+    ws.fill_(0xFF)          # every float in it reads as NaN
+    o, lse = attn.attn_decode(*args, Hkv=2, num_splits=64, with_lse=True,
+                              workspace=ws)
+    o2, l2 = attn.attn_decode(*args, Hkv=2, num_splits=64, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    assert torch.isfinite(o.float()).all()
+
+
 @pytest.mark.parametrize("sigma", [0.01, 4.0])
 def test_decode_value_scale(sigma):
     check_decode([100, 1500], 8, 2, 128, sigma=sigma, seed=9)
