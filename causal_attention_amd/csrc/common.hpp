@@ -84,6 +84,15 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
+// x combined with its value in the other half of the wave (lane ^ 32) by
+// max or +, with one v_permlane32_swap (no LDS traffic).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(
+      __builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+      false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+               __builtin_bit_cast(float, (unsigned)r[1]));
+}
 
 // s_waitcnt vmcnt(N): at most N vector-memory loads of this wave in flight
 // (they complete in issue order).

@@ -233,15 +233,33 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   // Issue the direct loads of key tile jt into (Kd, Vd).  Rows past the end
   // of the sequence load row S-1 (their scores are masked to -inf, so their
   // values are multiplied by p = 0).
+  unsigned koffb[IPW], voffb[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int row = (w * IPW + i) * RPI + lane / CPR, pos = lane % CPR;
+    koffb[i] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2;
+    voffb[i] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2;
+  }
   auto issue_tile = [&](int jt, __bf16* Kd, __bf16* Vd) {
     const int j0 = jt * BN;
+    const char* Kb = reinterpret_cast<const char*>(Kp + (size_t)j0 * D);
+    const char* Vb = reinterpret_cast<const char*>(Vp + (size_t)j0 * D);
+    if (j0 + BN <= S) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int r0 = (w * IPW + i) * RPI;
-      const int row = r0 + lane / CPR, pos = lane % CPR;
-      const size_t grow = (size_t)min(j0 + row, S - 1) * D;
-      lds_direct_load16(Kp + grow + 8 * swz_k<CPR>(row, pos), Kd + r0 * D);
-      lds_direct_load16(Vp + grow + 8 * swz_v<CPR>(row, pos), Vd + r0 * D);
+      for (int i = 0; i < IPW; ++i) {
+        const int r0 = (w * IPW + i) * RPI;
+        lds_direct_load16(Kb + koffb[i], Kd + r0 * D);
+        lds_direct_load16(Vb + voffb[i], Vd + r0 * D);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int r0 = (w * IPW + i) * RPI;
+        const int row = r0 + lane / CPR;
+        const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
+        lds_direct_load16(Kb + koffb[i] + back, Kd + r0 * D);
+        lds_direct_load16(Vb + voffb[i] + back, Vd + r0 * D);
+      }
     }
   };
 
@@ -298,10 +316,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     return sum;
   };
   auto rowmax = [&](const f32x16& sv) {
-    float mx = sv[0];
+    float t[5];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-    return fmaxf(mx, swap_halves(mx)) * scale_log2;
+    for (int g = 0; g < 5; ++g)
+      t[g] = fmaxf(fmaxf(sv[3 * g], sv[3 * g + 1]), sv[3 * g + 2]);
+    const float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]),
+                           fmaxf(fmaxf(t[3], t[4]), sv[15]));
+    return max_halves(mx) * scale_log2;
   };
   auto rescale = [&](float m_new) {
     const float alpha = fast_exp2(m_i - m_new);
@@ -318,8 +339,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     if constexpr (MASK) apply_mask_block<CAUSAL>(s0, j0, hh, query, S);
     const float mx0 = rowmax(s0);
     if (mx0 > m_i + kLazyRescale) rescale(mx0);
-    // A row with no visible key yet keeps m = -inf and gets p = 0.
-    const float neg_m0 = (m_i == -INFINITY) ? 0.f : -m_i;
+    // Every row sees key 0, so m is finite from the first sub-block on.
+    const float neg_m0 = -m_i;
 
     f32x16 s1 = qk_sub(Kt, 1);
     bf16x8 pb0[2];
@@ -329,8 +350,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
       apply_mask_block<CAUSAL>(s1, j0 + 32, hh, query, S);
     const float mx1 = rowmax(s1);
     const bool up = mx1 > m_i + kLazyRescale;
-    const float m1 = up ? mx1 : m_i;
-    const float neg_m1 = (m1 == -INFINITY) ? 0.f : -m1;
+    const float neg_m1 = up ? -mx1 : -m_i;
 
     pv_sub(Vt, 0, pb0);
     bf16x8 pb1[2];
@@ -345,17 +365,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   // wave computes every tile of the range: a wave whose rows all lie above
   // a tile's keys gets p = 0 from the mask.
   const int n_full = min(min(n_kv, S / BN), CAUSAL ? (q_lo + 1) / BN : n_kv);
-  auto step = [&](auto mask_tag, int jt) {
+  auto step = [&](auto mask_tag, int jt, int buf) {
     wait_vmem();                  // this wave's loads of tile jt landed
     __syncthreads();              // everyone's landed; tile jt-1 consumed
-    __bf16* cur = smem + (jt & 1) * 2 * TILE;
-    __bf16* nxt = smem + ((jt + 1) & 1) * 2 * TILE;
+    __bf16* cur = smem + buf * 2 * TILE;
+    __bf16* nxt = smem + (buf ^ 1) * 2 * TILE;
     if (jt + 1 < n_kv) issue_tile(jt + 1, nxt, nxt + TILE);
     tile_body(mask_tag, jt * BN, cur, cur + TILE);
   };
   if (n_kv > 0) issue_tile(0, smem, smem + TILE);
-  for (int jt = 0; jt < n_full; ++jt) step(std::false_type{}, jt);
-  for (int jt = n_full; jt < n_kv; ++jt) step(std::true_type{}, jt);
+  // Two tiles per iteration so that the buffer of each is a constant.
+  int jt = 0;
+  for (; jt < n_full; jt += 2) {
+    step(std::false_type{}, jt, 0);
+    if (jt + 1 < n_full) step(std::false_type{}, jt + 1, 1);
+  }
+  for (jt = n_full; jt < n_kv; ++jt) step(std::true_type{}, jt, jt & 1);
 
   // Epilogue: O = acc / l (bf16, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
