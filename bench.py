@@ -255,7 +255,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_prefill_bf16_kernel",
+            "kernel": "attn_prefill_kernel",
             "achieved": round(p_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

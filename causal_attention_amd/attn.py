@@ -45,6 +45,8 @@ def lib():
             ctypes.c_size_t
         L.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.attn_prefill.restype = i
+        L.attn_prefill_f16.argtypes = L.attn_prefill.argtypes
+        L.attn_prefill_f16.restype = i
         L.attn_prefill_f32.argtypes = L.attn_prefill.argtypes
         L.attn_prefill_f32.restype = i
         L.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
@@ -54,6 +56,8 @@ def lib():
         L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
                                   vp, sz, vp]
         L.attn_decode.restype = i
+        L.attn_decode_f16.argtypes = L.attn_decode.argtypes
+        L.attn_decode_f16.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -85,18 +89,23 @@ def _check(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+_PREFILL_FN = {torch.bfloat16: "attn_prefill", torch.float16: "attn_prefill_f16",
+               torch.float32: "attn_prefill_f32"}
+_DECODE_FN = {torch.bfloat16: "attn_decode", torch.float16: "attn_decode_f16"}
+
+
 def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
                  with_lse=True):
     """Fused prefill attention.
 
-    q [B,Hq,S,D]; k, v [B,Hkv,S,D]; bf16 (calls ``attn_prefill``) or fp32
-    (calls ``attn_prefill_f32``).  Returns (o, lse) with o like q and lse
-    fp32 [B,Hq,S] (None when ``with_lse`` is False).  ``scale`` defaults to
-    1/sqrt(D).
+    q [B,Hq,S,D]; k, v [B,Hkv,S,D]; bf16 (calls ``attn_prefill``), fp16
+    (``attn_prefill_f16``) or fp32 (``attn_prefill_f32``).  Returns (o, lse)
+    with o like q and lse fp32 [B,Hq,S] (None when ``with_lse`` is False).
+    ``scale`` defaults to 1/sqrt(D).
     """
     dtype = q.dtype
-    if dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("q must be bfloat16 or float32")
+    if dtype not in _PREFILL_FN:
+        raise ValueError("q must be bfloat16, float16 or float32")
     _check(q, "q", dtype, 4)
     _check(k, "k", dtype, 4)
     _check(v, "v", dtype, 4)
@@ -117,8 +126,7 @@ def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
         _check(lse, "lse", torch.float32, 3)
         if lse.shape != (B, Hq, S):
             raise ValueError("lse must be [B,Hq,S]")
-    fn = lib().attn_prefill if dtype == torch.bfloat16 else \
-        lib().attn_prefill_f32
+    fn = getattr(lib(), _PREFILL_FN[dtype])
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
             D, float(scale), int(bool(causal)), _stream())
     if st != 0:
@@ -147,14 +155,18 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
                 out=None, with_lse=False, lse=None, workspace=None):
     """Split-K decode attention over a packed per-sequence KV cache.
 
-    q [B,Hq,D] bf16; kcache, vcache flat bf16 caches where sequence b is a
+    q [B,Hq,D] bf16 (calls ``attn_decode``) or fp16 (``attn_decode_f16``);
+    kcache, vcache flat caches of q's dtype where sequence b is a
     [Hkv, L_b, D] block; seqlens int32 [B] on the GPU.  Returns (o, lse);
     lse is fp32 [B,Hq] or None.  ``workspace`` (uint8 GPU tensor, see
     ``new_decode_workspace``) is allocated when not given.
     """
-    _check(q, "q", torch.bfloat16, 3)
-    _check(kcache, "kcache", torch.bfloat16, None)
-    _check(vcache, "vcache", torch.bfloat16, None)
+    dtype = q.dtype
+    if dtype not in _DECODE_FN:
+        raise ValueError("q must be bfloat16 or float16")
+    _check(q, "q", dtype, 3)
+    _check(kcache, "kcache", dtype, None)
+    _check(vcache, "vcache", dtype, None)
     _check(seqlens, "seqlens", torch.int32, 1)
     B, Hq, D = q.shape
     if seqlens.shape[0] != B:
@@ -165,7 +177,7 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", torch.bfloat16, 3)
+    _check(out, "out", dtype, 3)
     if with_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
@@ -174,12 +186,12 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
     if workspace is None:
         workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
     _check(workspace, "workspace", torch.uint8, 1)
-    st = lib().attn_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens),
-                           _ptr(out), B, Hq, Hkv, D, float(scale),
-                           int(num_splits), _ptr(lse), _ptr(workspace),
-                           workspace.numel(), _stream())
+    fn = getattr(lib(), _DECODE_FN[dtype])
+    st = fn(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B,
+            Hq, Hkv, D, float(scale), int(num_splits), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
-        raise AttnError(st, "attn_decode")
+        raise AttnError(st, _DECODE_FN[dtype])
     return out, lse
 
 
@@ -218,22 +230,27 @@ def prepare_prefill(q, k, v, out, lse=None, causal=True, scale=None):
             raise ValueError("lse must be [B,Hq,S]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    fn = lib().attn_prefill if dtype == torch.bfloat16 else \
-        lib().attn_prefill_f32
+    if dtype not in _PREFILL_FN:
+        raise ValueError("q must be bfloat16, float16 or float32")
+    fn = getattr(lib(), _PREFILL_FN[dtype])
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
             D, ctypes.c_float(scale), int(bool(causal)), _stream())
-    return PreparedCall(fn, fn.__name__, args, (q, k, v, out, lse))
+    return PreparedCall(fn, _PREFILL_FN[dtype], args, (q, k, v, out, lse))
 
 
 def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
                    num_splits=0, lse=None, scale=None):
-    """A PreparedCall of attn_decode on the current stream (arguments as for
-    ``attn_decode``; ``out`` and ``workspace`` are required)."""
-    _check(q, "q", torch.bfloat16, 3)
-    _check(kcache, "kcache", torch.bfloat16, None)
-    _check(vcache, "vcache", torch.bfloat16, None)
+    """A PreparedCall of attn_decode / attn_decode_f16 on the current stream
+    (arguments as for ``attn_decode``; ``out`` and ``workspace`` are
+    required)."""
+    dtype = q.dtype
+    if dtype not in _DECODE_FN:
+        raise ValueError("q must be bfloat16 or float16")
+    _check(q, "q", dtype, 3)
+    _check(kcache, "kcache", dtype, None)
+    _check(vcache, "vcache", dtype, None)
     _check(seqlens, "seqlens", torch.int32, 1)
-    _check(out, "out", torch.bfloat16, 3)
+    _check(out, "out", dtype, 3)
     _check(workspace, "workspace", torch.uint8, 1)
     if lse is not None:
         _check(lse, "lse", torch.float32, 2)
@@ -243,5 +260,6 @@ def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
     args = (_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B,
             Hq, Hkv, D, ctypes.c_float(scale), int(num_splits), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream())
-    return PreparedCall(lib().attn_decode, "attn_decode", args,
-                        (q, kcache, vcache, seqlens, out, workspace, lse))
+    return PreparedCall(getattr(lib(), _DECODE_FN[dtype]), _DECODE_FN[dtype],
+                        args, (q, kcache, vcache, seqlens, out, workspace,
+                               lse))

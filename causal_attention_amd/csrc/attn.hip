@@ -86,14 +86,18 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-template <int D, bool C>
-struct Bf16Prefill {
-  static void run(dim3 g, dim3 b, hipStream_t st, const __bf16* q,
-                  const __bf16* k, const __bf16* v, __bf16* o, float* lse,
-                  int B, int Hq, int Hkv, int S, float sl2, int nq, int ncu) {
-    hipLaunchKernelGGL((attn::attn_prefill_bf16_kernel<D, C>), g, b, 0, st, q,
-                       k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
-  }
+// 16-bit inputs (bf16 or fp16): the MFMA kernel for element type T.
+template <typename T>
+struct Half16Prefill {
+  template <int D, bool C>
+  struct L {
+    static void run(dim3 g, dim3 b, hipStream_t st, const T* q, const T* k,
+                    const T* v, T* o, float* lse, int B, int Hq, int Hkv,
+                    int S, float sl2, int nq, int ncu) {
+      hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st,
+                         q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
+    }
+  };
 };
 
 template <int D, bool C>
@@ -148,35 +152,94 @@ DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int P) {
   return w;
 }
 
-template <int D, int G>
-void launch_decode_dg(const __bf16* q, const __bf16* kc, const __bf16* vc,
-                      const int* seqlens, __bf16* o, float* lse, float* ws_o,
+template <typename T, int D, int G>
+void launch_decode_dg(const T* q, const T* kc, const T* vc,
+                      const int* seqlens, T* o, float* lse, float* ws_o,
                       float* ws_lse, int2* ws_seg, long long* ws_total, int B,
                       int Hkv, int P, float sl2, hipStream_t st) {
-  hipLaunchKernelGGL((attn::attn_decode_split_kernel<D, G>), dim3(P), dim3(64),
-                     0, st, q, kc, vc, seqlens, o, lse, ws_o, ws_lse, ws_seg,
-                     ws_total, B, Hkv, P, sl2);
-  hipLaunchKernelGGL((attn::attn_decode_combine_kernel<D, G>),
+  hipLaunchKernelGGL((attn::attn_decode_split_kernel<T, D, G>), dim3(P),
+                     dim3(64), 0, st, q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                     ws_seg, ws_total, B, Hkv, P, sl2);
+  hipLaunchKernelGGL((attn::attn_decode_combine_kernel<T, D, G>),
                      dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, ws_seg,
                      ws_total, o, lse, Hkv, P);
 }
 
-template <int D>
-void launch_decode_d(int G, const __bf16* q, const __bf16* kc,
-                     const __bf16* vc, const int* seqlens, __bf16* o,
-                     float* lse, float* ws_o, float* ws_lse, int2* ws_seg,
-                     long long* ws_total, int B, int Hkv, int P, float sl2,
-                     hipStream_t st) {
+template <typename T, int D>
+void launch_decode_d(int G, const T* q, const T* kc, const T* vc,
+                     const int* seqlens, T* o, float* lse, float* ws_o,
+                     float* ws_lse, int2* ws_seg, long long* ws_total, int B,
+                     int Hkv, int P, float sl2, hipStream_t st) {
   switch (G) {
-    case 1: launch_decode_dg<D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
-    case 2: launch_decode_dg<D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
-    case 4: launch_decode_dg<D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                   ws_seg, ws_total, B, Hkv, P, sl2, st); break;
-    default: launch_decode_dg<D, 8>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                    ws_seg, ws_total, B, Hkv, P, sl2, st); break;
+    case 1: launch_decode_dg<T, D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+      break;
+    case 2: launch_decode_dg<T, D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+      break;
+    case 4: launch_decode_dg<T, D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
+                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+      break;
+    default: launch_decode_dg<T, D, 8>(q, kc, vc, seqlens, o, lse, ws_o,
+                                       ws_lse, ws_seg, ws_total, B, Hkv, P,
+                                       sl2, st);
+      break;
   }
+}
+
+// Shared body of the bf16 and fp16 prefill entry points.
+template <typename T>
+int prefill16(const void* q, const void* k, const void* v, void* o,
+              float* lse, int B, int Hq, int Hkv, int S, int D, float scale,
+              int causal, void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK || empty) return st;
+  return launch_prefill<T, Half16Prefill<T>::template L>(
+      static_cast<const T*>(q), static_cast<const T*>(k),
+      static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv, S, D,
+      scale, causal, stream);
+}
+
+template <typename T>
+int decode16(const void* q, const void* kcache, const void* vcache,
+                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                float scale, int num_splits, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
+  if (B == 0) return ATTN_OK;
+  if (!q || !kcache || !vcache || !seqlens || !o || !workspace)
+    return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) ||
+      !aligned(o, 16) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
+      !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  const int P = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  const DecodeWorkspace wl = decode_workspace(B, Hq, Hkv, D, P);
+  if (workspace_bytes < wl.bytes) return ATTN_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  float* ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+  float* ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+  int2* ws_seg = reinterpret_cast<int2*>(ws + wl.seg_off);
+  long long* ws_total = reinterpret_cast<long long*>(ws + wl.total_off);
+  const int G = Hq / Hkv;
+  const float sl2 = scale * attn::kLog2e;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const T* qb = static_cast<const T*>(q);
+  const T* kb = static_cast<const T*>(kcache);
+  const T* vb = static_cast<const T*>(vcache);
+  T* ob = static_cast<T*>(o);
+  if (D == 64)
+    launch_decode_d<T, 64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
+                           ws_seg, ws_total, B, Hkv, P, sl2, hs);
+  else
+    launch_decode_d<T, 128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
+                            ws_seg, ws_total, B, Hkv, P, sl2, hs);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -186,14 +249,15 @@ extern "C" {
 int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  float* lse, int B, int Hq, int Hkv, int S, int D,
                  float scale, int causal, void* stream) {
-  bool empty;
-  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
-                               &empty);
-  if (st != ATTN_OK || empty) return st;
-  return launch_prefill<__bf16, Bf16Prefill>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
-      S, D, scale, causal, stream);
+  return prefill16<__bf16>(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal,
+                           stream);
+}
+
+int attn_prefill_f16(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int Hq, int Hkv, int S, int D,
+                     float scale, int causal, void* stream) {
+  return prefill16<_Float16>(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal,
+                             stream);
 }
 
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
@@ -220,39 +284,17 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
                 const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
                 float scale, int num_splits, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
-  if (st != ATTN_OK) return st;
-  if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
-  if (B == 0) return ATTN_OK;
-  if (!q || !kcache || !vcache || !seqlens || !o || !workspace)
-    return ATTN_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) ||
-      !aligned(o, 16) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
-      !aligned(workspace, 16))
-    return ATTN_ERR_ALIGN;
-  const int P = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
-  const DecodeWorkspace wl = decode_workspace(B, Hq, Hkv, D, P);
-  if (workspace_bytes < wl.bytes) return ATTN_ERR_WORKSPACE;
+  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, scale,
+                          num_splits, lse, workspace, workspace_bytes, stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  float* ws_o = reinterpret_cast<float*>(ws + wl.o_off);
-  float* ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
-  int2* ws_seg = reinterpret_cast<int2*>(ws + wl.seg_off);
-  long long* ws_total = reinterpret_cast<long long*>(ws + wl.total_off);
-  const int G = Hq / Hkv;
-  const float sl2 = scale * attn::kLog2e;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const __bf16* qb = static_cast<const __bf16*>(q);
-  const __bf16* kb = static_cast<const __bf16*>(kcache);
-  const __bf16* vb = static_cast<const __bf16*>(vcache);
-  __bf16* ob = static_cast<__bf16*>(o);
-  if (D == 64)
-    launch_decode_d<64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                        ws_seg, ws_total, B, Hkv, P, sl2, hs);
-  else
-    launch_decode_d<128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                         ws_seg, ws_total, B, Hkv, P, sl2, hs);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
+                    const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                    float scale, int num_splits, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode16<_Float16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D,
+                            scale, num_splits, lse, workspace, workspace_bytes,
+                            stream);
 }
 
 const char* attn_status_string(int status) {

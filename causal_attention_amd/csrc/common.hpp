@@ -29,6 +29,45 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16-bit input elements: bf16 (the workloads' type) and fp16.  The kernels
+// are written once against these traits: the 8-element MFMA operand vector,
+// the 32x32x16 and 16x16x32 products with fp32 accumulation, and the
+// round-to-nearest-even conversion of two fp32 values to a packed pair.
+template <typename T>
+struct Elem16;
+
+template <>
+struct Elem16<__bf16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mma32(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <>
+struct Elem16<_Float16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mma32(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
 // fp32 variant: one contraction element per lane (lane half l/32 picks it).
 __device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
                                                    f32x16 c) {

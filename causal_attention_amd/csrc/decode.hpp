@@ -29,7 +29,8 @@
 //    (global_load_lds_dwordx4, 1 KB contiguous per instruction), the next
 //    block's loads are issued before the current one is multiplied, and no
 //    barrier is needed until the segment ends.
-//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (the heads
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (_f16 for
+//    fp16 inputs; the heads
 //    are MFMA columns, the other columns are zero): the A operand K comes from
 //    LDS rows, V^T from transposed LDS reads (ds_read_b64_tr_b16), and the
 //    probabilities stay in registers as the B operand of the second product.
@@ -47,10 +48,6 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kDecodeBlock = 32;                  // keys per block
 
-__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b,
-                                                    f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // T blocks cut into P equal contiguous ranges: range i starts at
 // floor(i*T/P) = q*i + floor(r*i/P) with T = q*P + r (r*i < P*P, so the
@@ -190,11 +187,11 @@ struct DecodeLayout {
 };
 
 // One wave per workgroup, one key range per wave.
-template <int D, int G>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(64) void attn_decode_split_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc,
-    const __bf16* __restrict__ Vc, const int* __restrict__ seqlens,
-    __bf16* __restrict__ O, float* __restrict__ LSE,
+    const T* __restrict__ Q, const T* __restrict__ Kc,
+    const T* __restrict__ Vc, const int* __restrict__ seqlens,
+    T* __restrict__ O, float* __restrict__ LSE,
     float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int2* __restrict__ ws_seg, long long* __restrict__ ws_total, int B,
     int Hkv, int P, float scale_log2) {
@@ -203,6 +200,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   constexpr int RPI = Lay::RPI, NKI = Lay::NKI, NQI = Lay::NQI;
   constexpr int BUF = Lay::BUF, KBYTES = Lay::KBYTES;
   static_assert(G <= 16, "heads are MFMA columns");
+  using E = Elem16<T>;
+  typedef typename E::x8 x8;
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[Lay::LDS];
 
@@ -218,14 +217,14 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   long long nblk = ch.bend;
   for (int base = 64; base < B; base += 64)
     nblk = load_chunk(seqlens, B, base, 0, nblk, lane).bend;
-  const long long T = nblk * Hkv;
-  const Ranges rg(T, P);
+  const long long total = nblk * Hkv;
+  const Ranges rg(total, P);
   const long long lo = rg.lo(wg), hi = rg.lo(wg + 1);
 
   // Workgroup 0: the block total for the combine kernel, and sequences
   // without keys (o = 0, lse = -inf, nothing to combine).
   if (wg == 0) {
-    if (lane == 0) *ws_total = T;
+    if (lane == 0) *ws_total = total;
     for (int base = 0; base < B; base += 64) {
       const int b = base + lane;
       if (b < B && seqlens[b] <= 0) {
@@ -385,9 +384,9 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
       sacc[kh] = f32x4{};
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        const bf16x8 qb = (c16 < G) ? __builtin_bit_cast(bf16x8, qv[t])
-                                    : bf16x8{};
-        sacc[kh] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kh][t]),
+        const x8 qb = (c16 < G) ? __builtin_bit_cast(x8, qv[t])
+                                    : x8{};
+        sacc[kh] = E::mma16(__builtin_bit_cast(x8, kv[kh][t]),
                                       qb, sacc[kh]);
       }
     }
@@ -415,17 +414,17 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
       m_ref = mx;
     }
     const float neg_m = -m_ref;
-    bf16x8 pB;
+    x8 pB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p = fast_exp2(fmaf(x[i], scale_log2, neg_m));
       l_i += p;
-      pB[i] = (__bf16)p;
+      pB[i] = (T)p;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const u32x4 a = {vlo[db][0], vlo[db][1], vhi[db][0], vhi[db][1]};
-      oacc[db] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pB,
+      oacc[db] = E::mma16(__builtin_bit_cast(x8, a), pB,
                                     oacc[db]);
     }
   };
@@ -465,8 +464,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           u32x2 pr;
-          pr[0] = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
-          pr[1] = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+          pr[0] = E::pack2(oacc[db][0] * inv, oacc[db][1] * inv);
+          pr[1] = E::pack2(oacc[db][2] * inv, oacc[db][3] * inv);
           *reinterpret_cast<u32x2*>(O + row * D + 16 * db + 4 * g4) = pr;
         }
         if (LSE != nullptr && g4 == 0) LSE[row] = lse;
@@ -497,11 +496,11 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
 // holding the pieces; a segment finished in one range, or a sequence without
 // keys, needs nothing here.  Pieces are taken 16 at a time, with their LSEs
 // and partial rows all in flight together.
-template <int D, int G>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(D) void attn_decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const int2* __restrict__ ws_seg, const long long* __restrict__ ws_total,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hkv, int P) {
+    T* __restrict__ O, float* __restrict__ LSE, int Hkv, int P) {
   constexpr int TB = 16;
   __shared__ float s_m[TB];
   const int j = blockIdx.x / G, h = blockIdx.x % G;
@@ -542,7 +541,7 @@ __global__ __launch_bounds__(D) void attn_decode_combine_kernel(
       o = fmaf(w, w > 0.f ? v[t] : 0.f, o);
     }
   }
-  O[orow * D + d] = (__bf16)(o / W);
+  O[orow * D + d] = (T)(o / W);
   if (LSE != nullptr && d == 0) LSE[orow] = M + logf(W);
 }
 

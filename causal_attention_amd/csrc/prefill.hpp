@@ -9,7 +9,8 @@
 // ragged tail block is loaded as zeros and its scores set to -inf).
 //
 // gfx950 mapping.  Each of the 4 waves owns 32 query rows.  Scores are formed
-// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are the A
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (_f16 for fp16
+// inputs): K rows are the A
 // operand (read from LDS), Q^T is the B operand (kept in VGPRs for the whole
 // tile), and the accumulator leaves each lane with ONE query (lane % 32) and
 // 16 keys per 32-key block.  Row max and row sum are then an in-lane
@@ -140,7 +141,7 @@ __device__ __forceinline__ void apply_mask_block(f32x16& x, int j0, int hh,
   }
 }
 
-// ---------------------------------------------------------------- bf16 path
+// ------------------------------------------------- bf16 / fp16 path
 //
 // K and V tiles go global -> LDS with gfx950's direct loads
 // (global_load_lds_dwordx4: no VGPR staging, each wave instruction fills 1 KB
@@ -166,13 +167,14 @@ __device__ __forceinline__ int swz_v(int row, int c) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+// Transposed 8-byte LDS read of 16-bit elements (any 16-bit type).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(u32x2, v);
 }
 
-__device__ __forceinline__ void lds_direct_load16(const void* g, __bf16* l) {
+__device__ __forceinline__ void lds_direct_load16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(
       g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
 }
@@ -180,10 +182,10 @@ __device__ __forceinline__ void lds_direct_load16(const void* g, __bf16* l) {
 // s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-    const __bf16* __restrict__ V, __bf16* __restrict__ O,
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K,
+    const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
     int n_qtiles, int n_cu) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
@@ -193,9 +195,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   constexpr int IPW = BN / RPI / 4;           // load instrs per wave per tile
   constexpr int TILE = BN * D;                // elements per K or V tile
   static_assert(IPW >= 1, "tile shape");
+  using E = Elem16<T>;
+  typedef typename E::x8 x8;
 
   // [buffer][K, V][TILE]
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];
 
   const int tid = threadIdx.x;
   // wave index as a uniform (scalar) value, so per-wave branches are scalar
@@ -203,9 +207,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const TileCoord tc =
       tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
-  const __bf16* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
-  const __bf16* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
-  const __bf16* Vp = V + (size_t)(tc.b * Hkv + tc.g) * S * D;
+  const T* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
+  const T* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
+  const T* Vp = V + (size_t)(tc.b * Hkv + tc.g) * S * D;
 
   const int q_lo = tc.qt * BM;
   const int q_hi = min(S, q_lo + BM);
@@ -215,14 +219,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   const int n_kv = (kv_end + BN - 1) / BN;
 
   // Q^T as the MFMA B operand: lane holds query `query`, dims 16t+8hh..+7.
-  bf16x8 qB[KT];
+  x8 qB[KT];
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
     if (query < S)
-      qB[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)query * D +
+      qB[t] = *reinterpret_cast<const x8*>(Qp + (size_t)query * D +
                                                16 * t + 8 * hh);
     else
-      qB[t] = bf16x8{};
+      qB[t] = x8{};
   }
 
   f32x16 oacc[NDB];
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     koffb[i] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2;
     voffb[i] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2;
   }
-  auto issue_tile = [&](int jt, __bf16* Kd, __bf16* Vd) {
+  auto issue_tile = [&](int jt, T* Kd, T* Vd) {
     const int j0 = jt * BN;
     const char* Kb = reinterpret_cast<const char*>(Kp + (size_t)j0 * D);
     const char* Vb = reinterpret_cast<const char*>(Vp + (size_t)j0 * D);
@@ -273,18 +277,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   const int grp = lane >> 4, jl = lane & 15;
   const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
   const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
-  auto qk_sub = [&](const __bf16* Kt, int kb) {
+  auto qk_sub = [&](const T* Kt, int kb) {
     f32x16 acc = f32x16{};
     const int row = kb * 32 + r;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+      const x8 a = *reinterpret_cast<const x8*>(
           Kt + row * D + 8 * swz_k<CPR>(row, 2 * t + hh));
-      acc = mfma_32x32x16_bf16(a, qB[t], acc);
+      acc = E::mma32(a, qB[t], acc);
     }
     return acc;
   };
-  auto pv_sub = [&](const __bf16* Vt, int kb, const bf16x8 (&pb)[2]) {
+  auto pv_sub = [&](const T* Vt, int kb, const x8 (&pb)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int row0 = kb * 32 + 16 * u + vrow_off;
@@ -292,18 +296,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
       for (int db = 0; db < NDB; ++db) {
         const int col = db * 32 + vcol_off;
         const int c = col >> 3, e = col & 7;
-        const bf16x4 lo = lds_read_tr16(Vt + row0 * D +
-                                        8 * swz_v<CPR>(row0, c) + e);
-        const bf16x4 hi = lds_read_tr16(Vt + (row0 + 8) * D +
-                                        8 * swz_v<CPR>(row0 + 8, c) + e);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3],
-                          hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = mfma_32x32x16_bf16(a, pb[u], oacc[db]);
+        const u32x2 lo = lds_read_tr16(Vt + row0 * D +
+                                       8 * swz_v<CPR>(row0, c) + e);
+        const u32x2 hi = lds_read_tr16(Vt + (row0 + 8) * D +
+                                       8 * swz_v<CPR>(row0 + 8, c) + e);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = E::mma32(__builtin_bit_cast(x8, a), pb[u], oacc[db]);
       }
     }
   };
-  // p = exp2(s*c + neg_m) as two bf16x8 B operands; returns the lane sum.
-  auto exp_sub = [&](const f32x16& sv, float neg_m, bf16x8 (&pb)[2]) {
+  // p = exp2(s*c + neg_m) as two x8 B operands; returns the lane sum.
+  auto exp_sub = [&](const f32x16& sv, float neg_m, x8 (&pb)[2]) {
     float sum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
       for (int i = 0; i < 8; ++i) {
         const float p = fast_exp2(fmaf(sv[8 * u + i], scale_log2, neg_m));
         sum += p;
-        pb[u][i] = (__bf16)p;
+        pb[u][i] = (T)p;
       }
     return sum;
   };
@@ -332,8 +335,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     m_i = m_new;
   };
 
-  auto tile_body = [&](auto mask_tag, int j0, const __bf16* Kt,
-                       const __bf16* Vt) {
+  auto tile_body = [&](auto mask_tag, int j0, const T* Kt,
+                       const T* Vt) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0 = qk_sub(Kt, 0);
     if constexpr (MASK) apply_mask_block<CAUSAL>(s0, j0, hh, query, S);
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     const float neg_m0 = -m_i;
 
     f32x16 s1 = qk_sub(Kt, 1);
-    bf16x8 pb0[2];
+    x8 pb0[2];
     l_i += exp_sub(s0, neg_m0, pb0);
 
     if constexpr (MASK)
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
     const float neg_m1 = up ? -mx1 : -m_i;
 
     pv_sub(Vt, 0, pb0);
-    bf16x8 pb1[2];
+    x8 pb1[2];
     const float sum1 = exp_sub(s1, neg_m1, pb1);
     if (up) rescale(mx1);
     l_i += sum1;
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   auto step = [&](auto mask_tag, int jt, int buf) {
     wait_vmem();                  // this wave's loads of tile jt landed
     __syncthreads();              // everyone's landed; tile jt-1 consumed
-    __bf16* cur = smem + buf * 2 * TILE;
-    __bf16* nxt = smem + (buf ^ 1) * 2 * TILE;
+    T* cur = smem + buf * 2 * TILE;
+    T* nxt = smem + (buf ^ 1) * 2 * TILE;
     if (jt + 1 < n_kv) issue_tile(jt + 1, nxt, nxt + TILE);
     tile_body(mask_tag, jt * BN, cur, cur + TILE);
   };
@@ -382,18 +385,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_bf16_kernel(
   }
   for (jt = n_full; jt < n_kv; ++jt) step(std::true_type{}, jt, jt & 1);
 
-  // Epilogue: O = acc / l (bf16, RNE) and LSE = (m_ref + log2 l) * ln 2.
+  // Epilogue: O = acc / l (input type, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
   if (query < S) {
     const float inv = 1.f / l_tot;
-    __bf16* orow = O + (size_t)(tc.b * Hq + tc.hq) * S * D + (size_t)query * D;
+    T* orow = O + (size_t)(tc.b * Hq + tc.hq) * S * D + (size_t)query * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         u32x2 pr;
-        pr[0] = pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv);
-        pr[1] = pack_bf16x2(oacc[db][4 * a + 2] * inv,
+        pr[0] = E::pack2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv);
+        pr[1] = E::pack2(oacc[db][4 * a + 2] * inv,
                             oacc[db][4 * a + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hh) = pr;
       }

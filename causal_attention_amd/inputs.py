@@ -5,7 +5,8 @@ attention arithmetic, so both the HIP path's tests and the fp64 oracle can
 consume the same bytes.  Every workload draws from
 ``numpy.random.default_rng(seed)`` in a fixed order (decode: sequence lengths
 first, then q, k, v; prefill: q, k, v), standard normal scaled by ``sigma``,
-then rounds to the storage dtype (bf16 with round-to-nearest-even via torch).
+then rounds to the storage dtype (bf16 or fp16 with round-to-nearest-even via
+torch).
 
 Shapes follow the pages' setups: the single-head and 12-head MHA prefill runs
 of "Attention三算子融合实战：从Triton到CUDA的推理加速优化" (section 5.1: batch
@@ -29,7 +30,7 @@ class Workload:
     Hq: int
     Hkv: int
     D: int
-    dtype: str           # "f32" or "bf16"
+    dtype: str           # "f32", "bf16" or "f16"
     sigma: float
     seed: int = 0
     S: int = 0           # prefill sequence length
@@ -45,7 +46,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return _STORAGE[self.dtype]
 
 
 WORKLOADS = {
@@ -64,9 +65,12 @@ WORKLOADS = {
 }
 
 
+_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t if dtype == "f32" else t.to(torch.bfloat16)
+    return t if dtype == "f32" else t.to(_STORAGE[dtype])
 
 
 def prefill_inputs(B, Hq, Hkv, S, D, dtype="bf16", sigma=1.0, seed=0):

@@ -73,6 +73,18 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  float scale, int causal, void* stream);
 
 /*
+ * Prefill attention, fp16 storage.  Same arguments and layouts as
+ * attn_prefill with q, k, v, o in IEEE fp16.  The mixed-precision rule of
+ * the attention-fusion page, section 5.5, holds as for bf16: fp16 only in
+ * the stored tensors and the MFMA inputs (P is rounded to fp16 for the PV
+ * product), fp32 for the QK^T and PV accumulation and for every
+ * cross-iteration state (m, l, acc).  Errors as attn_prefill.
+ */
+int attn_prefill_f16(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int B, int Hq, int Hkv, int S, int D,
+                     float scale, int causal, void* stream);
+
+/*
  * Prefill attention, fp32 storage.  Same arguments and layouts as
  * attn_prefill with every tensor fp32.  The probabilities P stay fp32 (the
  * accuracy setting of the attention-fusion page, sections 3.3 and 5.5).
@@ -131,6 +143,16 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
                 const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
                 float scale, int num_splits, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention, fp16 storage: attn_decode with q, kcache, vcache and o
+ * in IEEE fp16 (attention-fusion page, section 5.5: fp16 storage, fp32
+ * accumulation and state).  Same layouts, workspace and errors.
+ */
+int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
+                    const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                    float scale, int num_splits, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* A static description of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);

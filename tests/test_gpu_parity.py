@@ -5,6 +5,14 @@ storage (fp32 accumulation inside the kernels), and 1e-3 on the natural-log
 LSE.  Inputs are seeded synthetic tensors; the oracle sees exactly the stored
 (bf16-rounded) values.
 
+fp16 storage (the mixed-precision rule of the attention-fusion page, section
+5.5: fp16 only in storage and MFMA inputs, fp32 accumulation and state) has no
+bound in the pages; it is derived from the arithmetic like the sigma sweep:
+P is rounded to fp16 before the PV product and O once more on output, each a
+relative error of at most 2^-11 on values bounded by max|v| (about 4.5 for
+unit-variance inputs at these sizes), so 2 * 4.5 * 2^-11 = 4.4e-3; the test
+uses 5e-3 per unit sigma.
+
 The 1e-5 / 2e-2 bounds are for unit-variance inputs.  For the input-scale
 sweep (sigma != 1) the bound is derived from the arithmetic, see ``o_tol``:
 with bf16 storage the error is the relative rounding of P and O (2^-9), so it
@@ -30,7 +38,7 @@ LSE_TOL = 1e-3
 
 def o_tol(dtype, sigma=1.0):
     s = max(1.0, sigma)
-    return 1e-5 * s ** 3 if dtype == "f32" else 2e-2 * s
+    return {"f32": 1e-5 * s ** 3, "bf16": 2e-2 * s, "f16": 5e-3 * s}[dtype]
 
 
 def say(*a):
@@ -154,12 +162,13 @@ def test_prefill_without_lse():
 
 # -------------------------------------------------------------------- decode
 
-def run_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
-    say(f"[decode] B={len(seqlens)} Hq={Hq} Hkv={Hkv} D={D} "
+def run_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0,
+               dtype="bf16"):
+    say(f"[decode] B={len(seqlens)} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
         f"ns={num_splits} sum(L)={int(np.sum(seqlens))} seed={seed}")
     sl, q, kc, vc = inputs.decode_inputs(len(seqlens), Hq, Hkv, D,
                                          seqlens=seqlens, sigma=sigma,
-                                         seed=seed)
+                                         seed=seed, dtype=dtype)
     o, lse = attn.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV),
                               torch.from_numpy(sl).to(DEV), Hkv=Hkv,
                               num_splits=num_splits, with_lse=True)
@@ -167,9 +176,10 @@ def run_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
     return sl, q, kc, vc, o, lse
 
 
-def check_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
+def check_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0,
+                 dtype="bf16"):
     sl, q, kc, vc, o, lse = run_decode(seqlens, Hq, Hkv, D, num_splits,
-                                       sigma, seed)
+                                       sigma, seed, dtype)
     ro, rl = oracle.decode(np64(q), np64(kc), np64(vc), sl, 1 / math.sqrt(D),
                            Hkv)
     go, gl = np64(o), lse.cpu().numpy()
@@ -180,7 +190,7 @@ def check_decode(seqlens, Hq, Hkv, D, num_splits=0, sigma=1.0, seed=0):
         eo = np.abs(go[live] - ro[live]).max()
         el = np.abs(gl[live] - rl[live]).max()
         say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-        assert eo <= o_tol("bf16", sigma) and el <= LSE_TOL
+        assert eo <= o_tol(dtype, sigma) and el <= LSE_TOL
     return o, lse
 
 
@@ -295,3 +305,35 @@ def test_decode_is_deterministic():
     o2, l2 = attn.attn_decode(*args, Hkv=2, with_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- fp16 path
+
+@pytest.mark.parametrize("S", [1, 65, 129, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (8, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_edge_shapes_f16(S, D, Hq, Hkv, causal):
+    check_prefill(1, Hq, Hkv, S, D, "f16", causal)
+
+
+def test_c3_shape_f16():
+    check_prefill(4, 8, 2, 2048, 128, "f16", True)
+
+
+@pytest.mark.parametrize("sigma", [0.01, 4.0])
+def test_prefill_value_scale_f16(sigma):
+    check_prefill(1, 8, 2, 300, 128, "f16", True, sigma=sigma)
+
+
+@pytest.mark.parametrize("num_splits", [1, 7, 0])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_f16(num_splits, D):
+    check_decode([1, 15, 17, 255, 4096, 64, 0, 129], 8, 2, D, num_splits,
+                 dtype="f16")
+
+
+def test_c4_decode_f16():
+    w = inputs.WORKLOADS["c4_decode_b32"]
+    sl = inputs.decode_seqlens(w.B, w.lmin, w.lmax, w.seed)
+    check_decode(sl, w.Hq, w.Hkv, w.D, dtype="f16")
