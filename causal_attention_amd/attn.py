@@ -58,6 +58,11 @@ def lib():
         L.attn_decode.restype = i
         L.attn_decode_f16.argtypes = L.attn_decode.argtypes
         L.attn_decode_f16.restype = i
+        L.attn_decode_padded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
+                                         f, i, vp, vp, sz, vp]
+        L.attn_decode_padded.restype = i
+        L.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.attn_kv_append.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -192,6 +197,65 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
             _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise AttnError(st, _DECODE_FN[dtype])
+    return out, lse
+
+
+def attn_kv_append(k_new, v_new, kcache, vcache, seqlens):
+    """Append one token per sequence to a padded KV cache (in place).
+
+    k_new, v_new [B,Hkv,D]; kcache, vcache [B,Hkv,cap,D] of the same 16-bit
+    dtype; seqlens int32 [B] on the GPU, advanced by one for every sequence
+    that is not full.  Launches on the current stream (graph-capturable).
+    """
+    dtype = k_new.dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("k_new must be bfloat16 or float16")
+    _check(k_new, "k_new", dtype, 3)
+    _check(v_new, "v_new", dtype, 3)
+    _check(kcache, "kcache", dtype, 4)
+    _check(vcache, "vcache", dtype, 4)
+    _check(seqlens, "seqlens", torch.int32, 1)
+    B, Hkv, cap, D = kcache.shape
+    if (k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or
+            vcache.shape != kcache.shape or seqlens.shape[0] != B):
+        raise ValueError("inconsistent kv append shapes")
+    st = lib().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(kcache),
+                              _ptr(vcache), _ptr(seqlens), B, Hkv, D, cap,
+                              _stream())
+    if st != 0:
+        raise AttnError(st, "attn_kv_append")
+
+
+def attn_decode_padded(q, kcache, vcache, seqlens, num_splits=0, scale=None,
+                       out=None, with_lse=False, lse=None, workspace=None):
+    """Decode attention over a padded cache [B,Hkv,cap,D] (bf16), with
+    L_b = min(seqlens[b], cap); otherwise as ``attn_decode``."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(kcache, "kcache", torch.bfloat16, 4)
+    _check(vcache, "vcache", torch.bfloat16, 4)
+    _check(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, D = q.shape
+    Hkv, cap = kcache.shape[1], kcache.shape[2]
+    if kcache.shape != (B, Hkv, cap, D) or vcache.shape != kcache.shape:
+        raise ValueError("kcache, vcache must be [B,Hkv,cap,D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+    if workspace is None:
+        workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
+    _check(workspace, "workspace", torch.uint8, 1)
+    st = lib().attn_decode_padded(
+        _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B, Hq,
+        Hkv, D, cap, float(scale), int(num_splits), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise AttnError(st, "attn_decode_padded")
     return out, lse
 
 

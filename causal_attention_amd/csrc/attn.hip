@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "decode.hpp"
+#include "kvcache.hpp"
 #include "prefill.hpp"
 
 namespace {
@@ -156,10 +157,10 @@ template <typename T, int D, int G>
 void launch_decode_dg(const T* q, const T* kc, const T* vc,
                       const int* seqlens, T* o, float* lse, float* ws_o,
                       float* ws_lse, int2* ws_seg, long long* ws_total, int B,
-                      int Hkv, int P, float sl2, hipStream_t st) {
+                      int Hkv, int P, int cap, float sl2, hipStream_t st) {
   hipLaunchKernelGGL((attn::attn_decode_split_kernel<T, D, G>), dim3(P),
                      dim3(64), 0, st, q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                     ws_seg, ws_total, B, Hkv, P, sl2);
+                     ws_seg, ws_total, B, Hkv, P, cap, sl2);
   hipLaunchKernelGGL((attn::attn_decode_combine_kernel<T, D, G>),
                      dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, ws_seg,
                      ws_total, o, lse, Hkv, P);
@@ -169,20 +170,23 @@ template <typename T, int D>
 void launch_decode_d(int G, const T* q, const T* kc, const T* vc,
                      const int* seqlens, T* o, float* lse, float* ws_o,
                      float* ws_lse, int2* ws_seg, long long* ws_total, int B,
-                     int Hkv, int P, float sl2, hipStream_t st) {
+                     int Hkv, int P, int cap, float sl2, hipStream_t st) {
   switch (G) {
     case 1: launch_decode_dg<T, D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+                                      ws_seg, ws_total, B, Hkv, P, cap, sl2,
+                                      st);
       break;
     case 2: launch_decode_dg<T, D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+                                      ws_seg, ws_total, B, Hkv, P, cap, sl2,
+                                      st);
       break;
     case 4: launch_decode_dg<T, D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                                      ws_seg, ws_total, B, Hkv, P, sl2, st);
+                                      ws_seg, ws_total, B, Hkv, P, cap, sl2,
+                                      st);
       break;
     default: launch_decode_dg<T, D, 8>(q, kc, vc, seqlens, o, lse, ws_o,
                                        ws_lse, ws_seg, ws_total, B, Hkv, P,
-                                       sl2, st);
+                                       cap, sl2, st);
       break;
   }
 }
@@ -202,11 +206,13 @@ int prefill16(const void* q, const void* k, const void* v, void* o,
       scale, causal, stream);
 }
 
+// Shared body of the decode entry points; cap = 0 for the packed cache, else
+// the per-sequence capacity of the padded cache.
 template <typename T>
 int decode16(const void* q, const void* kcache, const void* vcache,
-                const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
-                float scale, int num_splits, float* lse, void* workspace,
-                size_t workspace_bytes, void* stream) {
+             const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+             int cap, float scale, int num_splits, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
@@ -235,10 +241,10 @@ int decode16(const void* q, const void* kcache, const void* vcache,
   T* ob = static_cast<T*>(o);
   if (D == 64)
     launch_decode_d<T, 64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                           ws_seg, ws_total, B, Hkv, P, sl2, hs);
+                           ws_seg, ws_total, B, Hkv, P, cap, sl2, hs);
   else
     launch_decode_d<T, 128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                            ws_seg, ws_total, B, Hkv, P, sl2, hs);
+                            ws_seg, ws_total, B, Hkv, P, cap, sl2, hs);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -284,17 +290,57 @@ int attn_decode(const void* q, const void* kcache, const void* vcache,
                 const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
                 float scale, int num_splits, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, scale,
-                          num_splits, lse, workspace, workspace_bytes, stream);
+  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, 0,
+                          scale, num_splits, lse, workspace, workspace_bytes,
+                          stream);
 }
 
 int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
                     const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
                     float scale, int num_splits, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return decode16<_Float16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D,
+  return decode16<_Float16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, 0,
                             scale, num_splits, lse, workspace, workspace_bytes,
                             stream);
+}
+
+int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
+                       const int* seqlens, void* o, int B, int Hq, int Hkv,
+                       int D, int cap, float scale, int num_splits, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (cap <= 0) return B == 0 ? ATTN_OK : ATTN_ERR_SHAPE;
+  if ((long long)B * Hkv * cap > 0x7fffffffffffLL) return ATTN_ERR_SHAPE;
+  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, cap,
+                          scale, num_splits, lse, workspace, workspace_bytes,
+                          stream);
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
+                   void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
+                   void* stream) {
+  if (B < 0 || Hkv < 0 || cap < 0) return ATTN_ERR_SHAPE;
+  if (Hkv == 0) return ATTN_ERR_GQA;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (B == 0) return ATTN_OK;
+  if (cap == 0) return ATTN_ERR_SHAPE;
+  if (!k_new || !v_new || !kcache || !vcache || !seqlens) return ATTN_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kcache, 16) ||
+      !aligned(vcache, 16) || !aligned(seqlens, 4))
+    return ATTN_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const __bf16* kn = static_cast<const __bf16*>(k_new);
+  const __bf16* vn = static_cast<const __bf16*>(v_new);
+  __bf16* kc = static_cast<__bf16*>(kcache);
+  __bf16* vc = static_cast<__bf16*>(vcache);
+  if (D == 64)
+    hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 64>), dim3(B),
+                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
+                       seqlens, Hkv, cap);
+  else
+    hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 128>), dim3(B),
+                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
+                       seqlens, Hkv, cap);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 const char* attn_status_string(int status) {

@@ -81,9 +81,9 @@ __device__ __forceinline__ long long lane_i64(long long v, int l) {
 }
 
 // 64 consecutive sequences [base, base+64), one per lane: L (clamped to
-// >= 0), its 32-key block count, and the exclusive prefix sums of keys and of
-// blocks over all sequences before it.  kend / bend: the inclusive totals at
-// the end of the chunk (wave-uniform).
+// [0, cap] when cap > 0, else to >= 0), its 32-key block count, and the
+// exclusive prefix sums of keys and of blocks over all sequences before it.
+// kend / bend: the inclusive totals at the end of the chunk (wave-uniform).
 struct SeqChunk {
   int base;
   int L, nb;
@@ -92,12 +92,14 @@ struct SeqChunk {
 };
 
 __device__ __forceinline__ SeqChunk load_chunk(const int* __restrict__ seqlens,
-                                               int B, int base, long long k0,
-                                               long long b0, int lane) {
+                                               int B, int cap, int base,
+                                               long long k0, long long b0,
+                                               int lane) {
   SeqChunk c;
   c.base = base;
   const int b = base + lane;
   c.L = (b < B) ? max(seqlens[b], 0) : 0;
+  if (cap > 0) c.L = min(c.L, cap);
   c.nb = (c.L + kDecodeBlock - 1) / kDecodeBlock;
   long long ki = c.L, bi = c.nb;
 #pragma unroll
@@ -114,18 +116,6 @@ __device__ __forceinline__ SeqChunk load_chunk(const int* __restrict__ seqlens,
   c.kend = k0 + lane_i64(ki, 63);
   c.bend = b0 + lane_i64(bi, 63);
   return c;
-}
-
-// Total number of 32-key blocks over all sequences (one KV head).
-__device__ __forceinline__ long long total_blocks(const int* seqlens, int B,
-                                                  int lane) {
-  long long k0 = 0, b0 = 0;
-  for (int base = 0; base < B; base += 64) {
-    const SeqChunk c = load_chunk(seqlens, B, base, k0, b0, lane);
-    k0 = c.kend;
-    b0 = c.bend;
-  }
-  return b0;
 }
 
 // One (sequence b, KV head g) segment, as a range [s0, s0 + nb) in the global
@@ -194,7 +184,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     T* __restrict__ O, float* __restrict__ LSE,
     float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int2* __restrict__ ws_seg, long long* __restrict__ ws_total, int B,
-    int Hkv, int P, float scale_log2) {
+    int Hkv, int P, int cap, float scale_log2) {
   using Lay = DecodeLayout<D, G>;
   constexpr int KT = Lay::KT, NDB = Lay::NDB, CPR = Lay::CPR;
   constexpr int RPI = Lay::RPI, NKI = Lay::NKI, NQI = Lay::NQI;
@@ -213,10 +203,10 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   // The key blocks of every (sequence, KV head) segment, in order, and this
   // wave's range [lo, hi) of them.  For B <= 64 the first chunk of sequence
   // lengths is kept for the search below.
-  SeqChunk ch = load_chunk(seqlens, B, 0, 0, 0, lane);
+  SeqChunk ch = load_chunk(seqlens, B, cap, 0, 0, 0, lane);
   long long nblk = ch.bend;
   for (int base = 64; base < B; base += 64)
-    nblk = load_chunk(seqlens, B, base, 0, nblk, lane).bend;
+    nblk = load_chunk(seqlens, B, cap, base, 0, nblk, lane).bend;
   const long long total = nblk * Hkv;
   const Ranges rg(total, P);
   const long long lo = rg.lo(wg), hi = rg.lo(wg + 1);
@@ -251,7 +241,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
       g0 = (int)((lo - sb) / nbb);
       break;
     }
-    ch = load_chunk(seqlens, B, ch.base + 64, ch.kend, ch.bend, lane);
+    ch = load_chunk(seqlens, B, cap, ch.base + 64, ch.kend, ch.bend, lane);
   }
   DecodeSeg cur = make_seg(ch, lb, g0, Hkv, lo, hi);
 
@@ -272,7 +262,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
         return make_seg(ch, lb, 0, Hkv, lo, hi);
       }
       // blocks remain in the range, so a later chunk holds them
-      ch = load_chunk(seqlens, B, ch.base + 64, ch.kend, ch.bend, lane);
+      ch = load_chunk(seqlens, B, cap, ch.base + 64, ch.kend, ch.bend,
+                      lane);
       lb = -1;
     }
   };
@@ -295,7 +286,11 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   // segment's G query rows.
   auto issue = [&](const DecodeSeg& s, long long blk, int buf) {
     const int k0 = (int)(blk - s.s0) * kDecodeBlock;
-    const size_t seg_off = ((size_t)s.kx * Hkv + (size_t)s.g * s.L) * D;
+    // packed: sequence b at key offset kx, head g after g*L rows; padded
+    // (cap > 0): sequence b, head g at row (b*Hkv + g)*cap
+    const size_t seg_off =
+        cap > 0 ? ((size_t)s.b * Hkv + s.g) * (size_t)cap * D
+                : ((size_t)s.kx * Hkv + (size_t)s.g * s.L) * D;
     const char* Kp = reinterpret_cast<const char*>(Kc + seg_off);
     const char* Vp = reinterpret_cast<const char*>(Vc + seg_off);
     unsigned char* kb = lds + buf * BUF;

@@ -154,6 +154,38 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
                     float scale, int num_splits, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/*
+ * KV-cache append: the kv_cache_store step of the operator table of the
+ * Qwen3.5-0.8B page ("手写Triton kernel重构Qwen3.5-0.8B", section 2.2, row 18:
+ * write the new k/v into the KV cache), shaped for the CUDA Graph decode of
+ * that page's section 4 (preallocated buffers, positions on the device).
+ *   k_new, v_new  : [B, Hkv, D] 16-bit elements (bf16 or fp16; copied bit for
+ *                   bit), 16-byte aligned
+ *   kcache, vcache: [B, Hkv, cap, D] of the same type, the "padded" cache:
+ *                   sequence b holds seqlens[b] valid rows per KV head
+ *   seqlens       : DEVICE int32 [B].  For every b with
+ *                   0 <= seqlens[b] < cap, row seqlens[b] of each KV head of
+ *                   sequence b receives k_new / v_new and seqlens[b] is
+ *                   incremented; a full sequence is left unchanged.
+ * One launch on `stream`; nothing is read back to the host, so a decode step
+ * (append, then attn_decode_padded) can be captured once in a hipGraph and
+ * replayed step after step.  D must be 64 or 128; cap >= 1 when B > 0.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
+                   void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
+                   void* stream);
+
+/*
+ * Decode attention over the padded cache of attn_kv_append: attn_decode with
+ * kcache, vcache [B, Hkv, cap, D] bf16 and L_b = min(seqlens[b], cap).  Same
+ * q, o, lse, num_splits, workspace (attn_decode_workspace_size) and errors;
+ * cap <= 0 with B > 0 is ATTN_ERR_SHAPE.
+ */
+int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
+                       const int* seqlens, void* o, int B, int Hq, int Hkv,
+                       int D, int cap, float scale, int num_splits, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static description of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);
 
