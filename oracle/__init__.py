@@ -27,9 +27,13 @@ by page title and section:
 * "让编码智能体写 Triton 算子" (zmj.net/articles/3605), step 1: the reference is
   computed in float32 or float64, never in half precision.
 
-Pinned by ``tests/test_oracle.py`` (closed forms, brute force on tiny inputs,
-an fp64 library implementation, algebraic invariants).  No function here is
-"parity unpinned".
+``rope`` (``oracle/rotary.py``) rotates q and k before attention, following the
+"triton-optimization" skill page, section 3.4 (fused RoPE: rotate pairs
+(x[i], x[i + D/2]) by position-dependent angles).
+
+Pinned by ``tests/test_oracle.py`` and ``tests/test_oracle_rope.py`` (closed
+forms, brute force on tiny inputs, an fp64 library implementation, algebraic
+invariants, planted mistakes).  No function here is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -39,3 +43,4 @@ from .attention import (  # noqa: F401
     lse_combine,
     softmax_probabilities,
 )
+from .rotary import rope  # noqa: F401
