@@ -59,10 +59,13 @@ def lib():
         L.attn_decode_f16.argtypes = L.attn_decode.argtypes
         L.attn_decode_f16.restype = i
         L.attn_decode_padded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
-                                         f, i, vp, vp, sz, vp]
+                                         f, i, vp, f, vp, sz, vp]
         L.attn_decode_padded.restype = i
-        L.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp]
         L.attn_kv_append.restype = i
+        L.attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                        i, f, i, f, vp]
+        L.attn_prefill_rope.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -200,12 +203,47 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
     return out, lse
 
 
-def attn_kv_append(k_new, v_new, kcache, vcache, seqlens):
+def attn_prefill_rope(q, k, v, rope_base, causal=True, scale=None, out=None,
+                      lse=None, with_lse=True, k_rot=None):
+    """Prefill attention of RoPE(q), RoPE(k), v at positions 0..S-1 (bf16).
+
+    Returns (o, lse, k_rot) where k_rot [B,Hkv,S,D] holds the rotated keys
+    (allocated when not given).  See ``attn_prefill_rope`` in attn.h.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 4)
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    _check(k_rot, "k_rot", torch.bfloat16, 4)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+    st = lib().attn_prefill_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(lse), _ptr(k_rot), B, Hq, Hkv, S, D,
+                                 float(scale), int(bool(causal)),
+                                 float(rope_base), _stream())
+    if st != 0:
+        raise AttnError(st, "attn_prefill_rope")
+    return out, lse, k_rot
+
+
+def attn_kv_append(k_new, v_new, kcache, vcache, seqlens, rope_base=0.0):
     """Append one token per sequence to a padded KV cache (in place).
 
     k_new, v_new [B,Hkv,D]; kcache, vcache [B,Hkv,cap,D] of the same 16-bit
     dtype; seqlens int32 [B] on the GPU, advanced by one for every sequence
-    that is not full.  Launches on the current stream (graph-capturable).
+    that is not full.  ``rope_base`` > 0 stores k rotated to its position.
+    Launches on the current stream (graph-capturable).
     """
     dtype = k_new.dtype
     if dtype not in (torch.bfloat16, torch.float16):
@@ -221,15 +259,17 @@ def attn_kv_append(k_new, v_new, kcache, vcache, seqlens):
         raise ValueError("inconsistent kv append shapes")
     st = lib().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(kcache),
                               _ptr(vcache), _ptr(seqlens), B, Hkv, D, cap,
-                              _stream())
+                              float(rope_base), _stream())
     if st != 0:
         raise AttnError(st, "attn_kv_append")
 
 
 def attn_decode_padded(q, kcache, vcache, seqlens, num_splits=0, scale=None,
-                       out=None, with_lse=False, lse=None, workspace=None):
+                       out=None, with_lse=False, lse=None, workspace=None,
+                       rope_base=0.0):
     """Decode attention over a padded cache [B,Hkv,cap,D] (bf16), with
-    L_b = min(seqlens[b], cap); otherwise as ``attn_decode``."""
+    L_b = min(seqlens[b], cap); otherwise as ``attn_decode``.  ``rope_base``
+    > 0 rotates each query to its position L_b - 1 in the kernel."""
     _check(q, "q", torch.bfloat16, 3)
     _check(kcache, "kcache", torch.bfloat16, 4)
     _check(vcache, "vcache", torch.bfloat16, 4)
@@ -253,7 +293,7 @@ def attn_decode_padded(q, kcache, vcache, seqlens, num_splits=0, scale=None,
     st = lib().attn_decode_padded(
         _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B, Hq,
         Hkv, D, cap, float(scale), int(num_splits), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream())
+        float(rope_base), _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise AttnError(st, "attn_decode_padded")
     return out, lse

@@ -59,10 +59,23 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o,
   return ATTN_OK;
 }
 
+// Per-pair RoPE rates in turns per position, base^(-2i/D) / (2 pi), in fp64
+// (base = 0: RoPE off, all rates 0).
+attn::RopeRates rope_rates(double base, int D) {
+  attn::RopeRates r = {};
+  if (base > 0.0)
+    for (int i = 0; i < D / 2 && i < 64; ++i)
+      r.r[i] = pow(base, -2.0 * i / D) / (2.0 * M_PI);
+  return r;
+}
+
+bool rope_base_ok(float base) { return isfinite(base) && base >= 0.f; }
+
 template <typename T, template <int, bool> class Launcher>
 int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
                    int B, int Hq, int Hkv, int S, int D, float scale,
-                   int causal, void* stream) {
+                   int causal, void* stream, int use_rope = 0,
+                   const attn::RopeRates& rope = attn::RopeRates{}) {
   const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
   const dim3 grid((unsigned)(B * Hq * n_qtiles));
   const dim3 block(kPrefillThreads);
@@ -72,17 +85,17 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   if (D == 64) {
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
-                              sl2, n_qtiles, ncu);
+                              sl2, n_qtiles, ncu, use_rope, rope);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles, ncu);
+                               S, sl2, n_qtiles, ncu, use_rope, rope);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles, ncu);
+                               S, sl2, n_qtiles, ncu, use_rope, rope);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                                S, sl2, n_qtiles, ncu);
+                                S, sl2, n_qtiles, ncu, use_rope, rope);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -94,9 +107,11 @@ struct Half16Prefill {
   struct L {
     static void run(dim3 g, dim3 b, hipStream_t st, const T* q, const T* k,
                     const T* v, T* o, float* lse, int B, int Hq, int Hkv,
-                    int S, float sl2, int nq, int ncu) {
+                    int S, float sl2, int nq, int ncu, int use_rope,
+                    const attn::RopeRates& rope) {
       hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st,
-                         q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
+                         q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu,
+                         use_rope, rope);
     }
   };
 };
@@ -105,7 +120,8 @@ template <int D, bool C>
 struct F32Prefill {
   static void run(dim3 g, dim3 b, hipStream_t st, const float* q,
                   const float* k, const float* v, float* o, float* lse, int B,
-                  int Hq, int Hkv, int S, float sl2, int nq, int ncu) {
+                  int Hq, int Hkv, int S, float sl2, int nq, int ncu,
+                  int /*use_rope*/, const attn::RopeRates& /*rope*/) {
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
                        k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
@@ -157,10 +173,11 @@ template <typename T, int D, int G>
 void launch_decode_dg(const T* q, const T* kc, const T* vc,
                       const int* seqlens, T* o, float* lse, float* ws_o,
                       float* ws_lse, int2* ws_seg, long long* ws_total, int B,
-                      int Hkv, int P, int cap, float sl2, hipStream_t st) {
+                      int Hkv, int P, int cap, float sl2, int use_rope,
+                      const attn::RopeRates& rope, hipStream_t st) {
   hipLaunchKernelGGL((attn::attn_decode_split_kernel<T, D, G>), dim3(P),
                      dim3(64), 0, st, q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
-                     ws_seg, ws_total, B, Hkv, P, cap, sl2);
+                     ws_seg, ws_total, B, Hkv, P, cap, sl2, use_rope, rope);
   hipLaunchKernelGGL((attn::attn_decode_combine_kernel<T, D, G>),
                      dim3(B * Hkv * G), dim3(D), 0, st, ws_o, ws_lse, ws_seg,
                      ws_total, o, lse, Hkv, P);
@@ -170,23 +187,24 @@ template <typename T, int D>
 void launch_decode_d(int G, const T* q, const T* kc, const T* vc,
                      const int* seqlens, T* o, float* lse, float* ws_o,
                      float* ws_lse, int2* ws_seg, long long* ws_total, int B,
-                     int Hkv, int P, int cap, float sl2, hipStream_t st) {
+                     int Hkv, int P, int cap, float sl2, int use_rope,
+                     const attn::RopeRates& rope, hipStream_t st) {
   switch (G) {
     case 1: launch_decode_dg<T, D, 1>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
                                       ws_seg, ws_total, B, Hkv, P, cap, sl2,
-                                      st);
+                                      use_rope, rope, st);
       break;
     case 2: launch_decode_dg<T, D, 2>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
                                       ws_seg, ws_total, B, Hkv, P, cap, sl2,
-                                      st);
+                                      use_rope, rope, st);
       break;
     case 4: launch_decode_dg<T, D, 4>(q, kc, vc, seqlens, o, lse, ws_o, ws_lse,
                                       ws_seg, ws_total, B, Hkv, P, cap, sl2,
-                                      st);
+                                      use_rope, rope, st);
       break;
     default: launch_decode_dg<T, D, 8>(q, kc, vc, seqlens, o, lse, ws_o,
                                        ws_lse, ws_seg, ws_total, B, Hkv, P,
-                                       cap, sl2, st);
+                                       cap, sl2, use_rope, rope, st);
       break;
   }
 }
@@ -212,7 +230,11 @@ template <typename T>
 int decode16(const void* q, const void* kcache, const void* vcache,
              const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
              int cap, float scale, int num_splits, float* lse,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream,
+             float rope_base = 0.f) {
+  if (!rope_base_ok(rope_base)) return ATTN_ERR_SCALE;
+  const attn::RopeRates rope = rope_rates(rope_base, D);
+  const int use_rope = rope_base > 0.f;
   int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_SCALE;
@@ -241,10 +263,12 @@ int decode16(const void* q, const void* kcache, const void* vcache,
   T* ob = static_cast<T*>(o);
   if (D == 64)
     launch_decode_d<T, 64>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                           ws_seg, ws_total, B, Hkv, P, cap, sl2, hs);
+                           ws_seg, ws_total, B, Hkv, P, cap, sl2, use_rope,
+                           rope, hs);
   else
     launch_decode_d<T, 128>(G, qb, kb, vb, seqlens, ob, lse, ws_o, ws_lse,
-                            ws_seg, ws_total, B, Hkv, P, cap, sl2, hs);
+                            ws_seg, ws_total, B, Hkv, P, cap, sl2, use_rope,
+                           rope, hs);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -264,6 +288,40 @@ int attn_prefill_f16(const void* q, const void* k, const void* v, void* o,
                      float scale, int causal, void* stream) {
   return prefill16<_Float16>(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal,
                              stream);
+}
+
+int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* k_rot, int B, int Hq, int Hkv, int S,
+                      int D, float scale, int causal, float rope_base,
+                      void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK) return st;
+  if (!rope_base_ok(rope_base) || !(rope_base > 0.f)) return ATTN_ERR_SCALE;
+  if (empty) return ATTN_OK;
+  if (!k_rot) return ATTN_ERR_NULL;
+  if (!aligned(k_rot, 16)) return ATTN_ERR_ALIGN;
+  const attn::RopeRates rope = rope_rates(rope_base, D);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // K rotated once (every query tile of its head reads it), into k_rot
+  const long long rows = (long long)B * Hkv * S;
+  const long long threads = rows * (D / 16);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  __bf16* kr = static_cast<__bf16*>(k_rot);
+  if (D == 64)
+    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<__bf16, 64>), grid,
+                       dim3(256), 0, hs, kb, kr, rows, S, rope);
+  else
+    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<__bf16, 128>), grid,
+                       dim3(256), 0, hs, kb, kr, rows, S, rope);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  // Q rotated on load inside the attention kernel
+  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
+      static_cast<const __bf16*>(q), kr, static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), lse, B, Hq, Hkv, S, D, scale, causal, stream,
+      1, rope);
 }
 
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
@@ -307,18 +365,22 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
 int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
                        const int* seqlens, void* o, int B, int Hq, int Hkv,
                        int D, int cap, float scale, int num_splits, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       float rope_base, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (cap <= 0) return B == 0 ? ATTN_OK : ATTN_ERR_SHAPE;
   if ((long long)B * Hkv * cap > 0x7fffffffffffLL) return ATTN_ERR_SHAPE;
   return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, cap,
                           scale, num_splits, lse, workspace, workspace_bytes,
-                          stream);
+                          stream, rope_base);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
                    void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
-                   void* stream) {
+                   float rope_base, void* stream) {
   if (B < 0 || Hkv < 0 || cap < 0) return ATTN_ERR_SHAPE;
+  if (!rope_base_ok(rope_base)) return ATTN_ERR_SCALE;
+  const attn::RopeRates rope = rope_rates(rope_base, D);
+  const int use_rope = rope_base > 0.f;
   if (Hkv == 0) return ATTN_ERR_GQA;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (B == 0) return ATTN_OK;
@@ -335,11 +397,11 @@ int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
   if (D == 64)
     hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 64>), dim3(B),
                        dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
-                       seqlens, Hkv, cap);
+                       seqlens, Hkv, cap, use_rope, rope);
   else
     hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 128>), dim3(B),
                        dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
-                       seqlens, Hkv, cap);
+                       seqlens, Hkv, cap, use_rope, rope);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

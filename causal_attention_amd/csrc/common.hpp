@@ -68,6 +68,27 @@ struct Elem16<_Float16> {
   }
 };
 
+// Rotary position embedding (half-split pairs (x[i], x[i + D/2]), angle
+// p * base^(-2i/D)): the rate of each pair in turns per position,
+// base^(-2i/D) / (2 pi), computed on the host in fp64 and passed by value.
+struct RopeRates {
+  double r[64];
+};
+
+// Rotate the pair (x1, x2) by the angle of position pos at rate r (turns per
+// position).  The turn count is reduced to [0, 1) in fp64, so long positions
+// keep their accuracy; sin and cos of the fraction come from v_sin_f32 /
+// v_cos_f32, which take their argument in turns; the rotation is fp32.
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, int pos,
+                                          double r) {
+  const double t = (double)pos * r;
+  const float f = (float)(t - floor(t));
+  const float c = __builtin_amdgcn_cosf(f), s = __builtin_amdgcn_sinf(f);
+  const float y1 = x1 * c - x2 * s;
+  x2 = x1 * s + x2 * c;
+  x1 = y1;
+}
+
 // fp32 variant: one contraction element per lane (lane half l/32 picks it).
 __device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
                                                    f32x16 c) {

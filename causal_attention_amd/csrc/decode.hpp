@@ -184,7 +184,8 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     T* __restrict__ O, float* __restrict__ LSE,
     float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int2* __restrict__ ws_seg, long long* __restrict__ ws_total, int B,
-    int Hkv, int P, int cap, float scale_log2) {
+    int Hkv, int P, int cap, float scale_log2, int use_rope,
+    RopeRates rope) {
   using Lay = DecodeLayout<D, G>;
   constexpr int KT = Lay::KT, NDB = Lay::NDB, CPR = Lay::CPR;
   constexpr int RPI = Lay::RPI, NKI = Lay::NKI, NQI = Lay::NQI;
@@ -194,6 +195,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   typedef typename E::x8 x8;
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[Lay::LDS];
+  __shared__ double s_rates[D / 2];          // RoPE rates (when use_rope)
 
   const int lane = threadIdx.x;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -324,6 +326,11 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
   // lane-partial sum, O^T rows 16db + 4g4 + i.
   f32x4 oacc[NDB];
   float m_ref = -INFINITY, l_i = 0.f;
+  // This piece's query rows as the B operand (read from LDS on the piece's
+  // first block, rotated there when RoPE is on, then kept).
+  u32x4 qkeep[KT];
+  if (use_rope)
+    for (int i = lane; i < D / 2; i += 64) s_rates[i] = rope.r[i];
 
   const unsigned lds_base = lds_addr(lds);
   // One block: keys k0 .. k0+31 of segment s, in buffer buf.
@@ -332,12 +339,15 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     const int k0 = (int)(blk - s.s0) * kDecodeBlock;
     // Q^T (B operand): column c16 = head c16 (zero for c16 >= G), dims
     // 32t + 8g4 .. +7.  K (A operand): rows 16kh + c16, same dims.
-    u32x4 qv[KT], kv[2][KT];
+    u32x4 kv[2][KT];
     const int qh = min(c16, G - 1);
+    const bool fresh = blk == s.a;           // first block of this piece
+    if (fresh) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-      lds_read_b128_async(qv[t], kb + 2 * KBYTES + qh * D * 2 +
-                                     (32 * t + 8 * g4) * 2);
+      for (int t = 0; t < KT; ++t)
+        lds_read_b128_async(qkeep[t], kb + 2 * KBYTES + qh * D * 2 +
+                                          (32 * t + 8 * g4) * 2);
+    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -363,9 +373,31 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     lds_wait_all();
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      lds_tie(qv[t]);
       lds_tie(kv[0][t]);
       lds_tie(kv[1][t]);
+    }
+    if (fresh) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) lds_tie(qkeep[t]);
+      // RoPE of the query at its position L - 1 (the newest token): the
+      // pair of dim d = 32t + 8g4 + e (t < KT/2) is d + D/2, held by the
+      // same lane in register t + KT/2.
+      if (use_rope) {
+#pragma unroll
+        for (int t = 0; t < KT / 2; ++t) {
+          x8 a = __builtin_bit_cast(x8, qkeep[t]);
+          x8 b = __builtin_bit_cast(x8, qkeep[t + KT / 2]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float x1 = (float)a[e], x2 = (float)b[e];
+            rope_pair(x1, x2, s.L - 1, s_rates[32 * t + 8 * g4 + e]);
+            a[e] = (T)x1;
+            b[e] = (T)x2;
+          }
+          qkeep[t] = __builtin_bit_cast(u32x4, a);
+          qkeep[t + KT / 2] = __builtin_bit_cast(u32x4, b);
+        }
+      }
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -379,7 +411,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
       sacc[kh] = f32x4{};
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        const x8 qb = (c16 < G) ? __builtin_bit_cast(x8, qv[t])
+        const x8 qb = (c16 < G) ? __builtin_bit_cast(x8, qkeep[t])
                                     : x8{};
         sacc[kh] = E::mma16(__builtin_bit_cast(x8, kv[kh][t]),
                                       qb, sacc[kh]);

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
-    int n_qtiles, int n_cu) {
+    int n_qtiles, int n_cu, int use_rope, RopeRates rope) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -227,6 +227,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
                                                16 * t + 8 * hh);
     else
       qB[t] = x8{};
+  }
+  // RoPE on load: the pair of dim d = 16t + 8hh + e (t < KT/2) is
+  // d + D/2, held by the same lane in register t + KT/2.
+  if (use_rope) {
+#pragma unroll
+    for (int t = 0; t < KT / 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x1 = (float)qB[t][e], x2 = (float)qB[t + KT / 2][e];
+        const double r = hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
+        rope_pair(x1, x2, query, r);
+        qB[t][e] = (T)x1;
+        qB[t + KT / 2][e] = (T)x2;
+      }
   }
 
   f32x16 oacc[NDB];
@@ -404,6 +418,39 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
       LSE[(size_t)(tc.b * Hq + tc.hq) * S + query] =
           (m_i + fast_log2(l_tot)) * kLn2;
   }
+}
+
+// RoPE of whole rows: x, y [rows, D] with row i at position i % S (the
+// [B, H, S, D] layout), y = x rotated (y may be x).  One thread per pair of
+// 16-byte chunks (c, c + D/16); the rates sit in LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_rope_rows_kernel(
+    const T* __restrict__ x, T* __restrict__ y, long long rows, int S,
+    RopeRates rope) {
+  using E = Elem16<T>;
+  typedef typename E::x8 x8;
+  constexpr int HC = D / 16;                 // chunk pairs per row
+  __shared__ double rates[D / 2];
+  for (int i = threadIdx.x; i < D / 2; i += 256) rates[i] = rope.r[i];
+  __syncthreads();
+  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * HC) return;
+  const long long row = id / HC;
+  const int c = (int)(id % HC);
+  const int pos = (int)(row % S);
+  const T* xr = x + row * D;
+  T* yr = y + row * D;
+  x8 a = *reinterpret_cast<const x8*>(xr + 8 * c);
+  x8 b = *reinterpret_cast<const x8*>(xr + D / 2 + 8 * c);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x1 = (float)a[e], x2 = (float)b[e];
+    rope_pair(x1, x2, pos, rates[8 * c + e]);
+    a[e] = (T)x1;
+    b[e] = (T)x2;
+  }
+  *reinterpret_cast<x8*>(yr + 8 * c) = a;
+  *reinterpret_cast<x8*>(yr + D / 2 + 8 * c) = b;
 }
 
 // ---------------------------------------------------------------- fp32 path

@@ -48,7 +48,8 @@ typedef enum {
   ATTN_ERR_WORKSPACE = -6, /* decode workspace smaller than required */
   ATTN_ERR_SPLITS = -7,    /* num_splits < 0 or > ATTN_MAX_SPLITS */
   ATTN_ERR_LAUNCH = -8,    /* the HIP runtime rejected a kernel launch */
-  ATTN_ERR_SCALE = -9      /* scale is not a finite positive number */
+  ATTN_ERR_SCALE = -9      /* scale is not a finite positive number (or a
+                              RoPE base is negative or not finite) */
 } attn_status;
 
 /* Largest num_splits attn_decode accepts. */
@@ -83,6 +84,29 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
 int attn_prefill_f16(const void* q, const void* k, const void* v, void* o,
                      float* lse, int B, int Hq, int Hkv, int S, int D,
                      float scale, int causal, void* stream);
+
+/*
+ * Prefill attention with rotary position embedding (RoPE) on q and k, bf16.
+ * Arguments as attn_prefill, plus:
+ *   k_rot    : [B, Hkv, S, D] bf16 output, owned by the caller: k rotated to
+ *              positions 0..S-1 (what a KV cache stores), then read by the
+ *              attention kernel.  Must not alias q, k, v or o.
+ *   rope_base: > 0 (e.g. 10000).  Pair i = (x[i], x[i + D/2]) of a head
+ *              vector at position p turns by p * rope_base^(-2i/D): the
+ *              half-split rotation of the "triton-optimization" page,
+ *              section 3.4, with the usual angle (the pages print none).
+ *              Otherwise ATTN_ERR_SCALE.
+ * q is rotated on load inside the attention kernel (the Qwen3.5-0.8B page,
+ * section 1.2: RoPE computed in fp32 while q and k are loaded, no cos/sin
+ * tensor); k is rotated once by a first launch into k_rot, because every
+ * query tile of its head reads it.  Angles are reduced to a fraction of a
+ * turn in fp64 and sin/cos taken in fp32; rotated values are rounded to bf16
+ * for the MFMA.  Two launches on `stream`.
+ */
+int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* k_rot, int B, int Hq, int Hkv, int S,
+                      int D, float scale, int causal, float rope_base,
+                      void* stream);
 
 /*
  * Prefill attention, fp32 storage.  Same arguments and layouts as
@@ -167,24 +191,35 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
  *                   0 <= seqlens[b] < cap, row seqlens[b] of each KV head of
  *                   sequence b receives k_new / v_new and seqlens[b] is
  *                   incremented; a full sequence is left unchanged.
+ *   rope_base     : 0 for a plain copy; > 0 to store k rotated by RoPE at
+ *                   its position seqlens[b] (the k_rope step of the same
+ *                   table, row 5, fused into the store), see
+ *                   attn_prefill_rope for the rotation.  Negative or
+ *                   non-finite: ATTN_ERR_SCALE.
  * One launch on `stream`; nothing is read back to the host, so a decode step
  * (append, then attn_decode_padded) can be captured once in a hipGraph and
  * replayed step after step.  D must be 64 or 128; cap >= 1 when B > 0.
  */
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
                    void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
-                   void* stream);
+                   float rope_base, void* stream);
 
 /*
  * Decode attention over the padded cache of attn_kv_append: attn_decode with
  * kcache, vcache [B, Hkv, cap, D] bf16 and L_b = min(seqlens[b], cap).  Same
  * q, o, lse, num_splits, workspace (attn_decode_workspace_size) and errors;
  * cap <= 0 with B > 0 is ATTN_ERR_SHAPE.
+ *   rope_base: 0 for none; > 0 rotates each query by RoPE at its position
+ *              L_b - 1 (it is the newest token) inside the kernel, as the
+ *              Qwen3.5-0.8B page (section 1.2) applies RoPE while loading q;
+ *              the cached keys are expected already rotated
+ *              (attn_kv_append with the same base).
  */
 int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
                        const int* seqlens, void* o, int B, int Hq, int Hkv,
                        int D, int cap, float scale, int num_splits, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       float rope_base, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* A static description of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);

@@ -341,6 +341,15 @@ def test_c4_decode_f16():
 
 # --------------------------------------- padded cache, append, graph replay
 
+def bf16_stored(x):
+    """x rounded to bf16 (RNE, straight from fp64), as float64: the value a
+    bf16 tensor or a bf16 MFMA operand holds.  With RoPE the rotated q and k
+    are such operands (and the cache stores rotated keys in bf16), so the
+    expected values round the oracle's fp64 rotation at that point."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(
+        torch.bfloat16).double().numpy()
+
+
 def padded_to_packed(kc, sl):
     """[B,Hkv,cap,D] padded cache with lengths sl -> the packed layout."""
     return np.concatenate([kc[b, :, :max(int(L), 0)].reshape(-1)
@@ -392,17 +401,25 @@ def test_decode_padded_matches_oracle(num_splits):
     assert eo <= 2e-2 and el <= LSE_TOL
 
 
-def test_decode_step_graph_replay():
+@pytest.mark.parametrize("rope_base", [0.0, 10000.0])
+def test_decode_step_graph_replay(rope_base):
     """append + decode captured once, replayed step after step with new k/v
     copied in between; every replay is checked against an eager decode and
-    against the oracle on the cache as it stands."""
+    against the oracle on the cache as it stands (with RoPE: the oracle's
+    own rotation of every key at its position and of q at L - 1)."""
     B, Hq, Hkv, D, cap, steps = 4, 8, 2, 128, 600, 5
-    say(f"[graph decode step] B={B} cap={cap} steps={steps}")
+    say(f"[graph decode step] B={B} cap={cap} steps={steps} rope={rope_base}")
     rng = np.random.default_rng(13)
     bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
     lens0 = np.array([0, 31, 256, 500], dtype=np.int32)
-    kc = bf(rng.standard_normal((B, Hkv, cap, D))).to(DEV)
+    # raw keys of every position; the cache holds them rotated (oracle
+    # rotation, rounded to bf16) when RoPE is on
+    kraw = rng.standard_normal((B, Hkv, cap, D))
+    kstore = kraw if rope_base == 0 else \
+        bf16_stored(oracle.rope(kraw, np.arange(cap), rope_base))
+    kc = bf(kstore).to(DEV)
     vc = bf(rng.standard_normal((B, Hkv, cap, D))).to(DEV)
+    kref = np64(kc)                       # the oracle's view of the cache
     sl = torch.from_numpy(lens0.copy()).to(DEV)
     q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
     kn = torch.empty(B, Hkv, D, dtype=torch.bfloat16, device=DEV)
@@ -412,8 +429,9 @@ def test_decode_step_graph_replay():
     ws = attn.new_decode_workspace(B, Hq, Hkv, D, 0, DEV)
 
     def step():
-        attn.attn_kv_append(kn, vn, kc, vc, sl)
-        attn.attn_decode_padded(q, kc, vc, sl, out=o, lse=lse, workspace=ws)
+        attn.attn_kv_append(kn, vn, kc, vc, sl, rope_base=rope_base)
+        attn.attn_decode_padded(q, kc, vc, sl, out=o, lse=lse, workspace=ws,
+                                rope_base=rope_base)
 
     # warm up on a side stream (capture requirement), then capture one step
     # and undo the warm-up's append on the host copy of the lengths
@@ -435,17 +453,99 @@ def test_decode_step_graph_replay():
         kn.copy_(bf(rng.standard_normal((B, Hkv, D))).to(DEV))
         vn.copy_(bf(rng.standard_normal((B, Hkv, D))).to(DEV))
         torch.cuda.synchronize()
+        pos = lens0 + t                   # where this step's key lands
+        knew = np64(kn)
+        for b in range(B):
+            kref[b, :, pos[b]] = knew[b] if rope_base == 0 else \
+                bf16_stored(oracle.rope(knew[b], pos[b], rope_base))
         g.replay()
         torch.cuda.synchronize()
         lens = sl.cpu().numpy()
         assert (lens == lens0 + t + 1).all()
-        eo, el = attn.attn_decode_padded(q, kc, vc, sl, with_lse=True)
+        eo, el = attn.attn_decode_padded(q, kc, vc, sl, with_lse=True,
+                                         rope_base=rope_base)
         torch.cuda.synchronize()
         assert torch.equal(o, eo) and torch.equal(lse, el)
-        ro, rl = oracle.decode(np64(q), padded_to_packed(np64(kc), lens),
+        if rope_base:
+            # the stored key of this step: the oracle's rotation, up to the
+            # bf16 rounding of the stored value
+            for b in range(B):
+                d = np.abs(np64(kc)[b, :, pos[b]] - kref[b, :, pos[b]])
+                assert d.max() <= 2 ** -8 * np.abs(kref[b, :, pos[b]]).max()
+        qref = np64(q) if rope_base == 0 else \
+            bf16_stored(oracle.rope(np64(q), (lens - 1)[:, None], rope_base))
+        ro, rl = oracle.decode(qref, padded_to_packed(kref, lens),
                                padded_to_packed(np64(vc), lens), lens,
                                1 / math.sqrt(D), Hkv)
         err = np.abs(np64(o) - ro).max()
         say(f"   replay {t}: lens={lens.tolist()} max|dO|={err:.3e}")
         assert err <= 2e-2
         assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
+
+
+# ------------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D", [(1, 8, 2, 300, 128),
+                                          (2, 12, 12, 129, 64),
+                                          (1, 1, 1, 1, 128),
+                                          (4, 8, 2, 2048, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_rope_matches_oracle(B, Hq, Hkv, S, D, causal):
+    base = 10000.0
+    say(f"[prefill rope] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 4)
+    o, lse, kr = attn.attn_prefill_rope(q.to(DEV), k.to(DEV), v.to(DEV), base,
+                                        causal=causal)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    qr = bf16_stored(oracle.rope(np64(q), pos, base))
+    krr = bf16_stored(oracle.rope(np64(k), pos, base))
+    # rotated keys: the oracle's rotation, stored in bf16 (a rotation that
+    # lands next to a rounding boundary may round to the neighbouring value)
+    assert np.abs(np64(kr) - krr).max() <= 2 ** -8 * np.abs(krr).max()
+    ro, rl = oracle.prefill(qr, krr, np64(v), 1 / math.sqrt(D), causal)
+    eo, el = np.abs(np64(o) - ro).max(), np.abs(lse.cpu().numpy() - rl).max()
+    say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= 2e-2 and el <= LSE_TOL
+
+
+def test_prefill_rope_long_positions_sampled():
+    """Angles at positions up to 8191: reduced in fp64, so late rows are as
+    accurate as early ones.  Sampled rows against the oracle."""
+    B, Hq, Hkv, S, D, base = 1, 2, 1, 8192, 128, 10000.0
+    say(f"[prefill rope long] S={S}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 6)
+    o, lse, kr = attn.attn_prefill_rope(q.to(DEV), k.to(DEV), v.to(DEV), base)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    krr = bf16_stored(oracle.rope(np64(k), pos, base))
+    assert np.abs(np64(kr) - krr).max() <= 2 ** -8 * np.abs(krr).max()
+    rows = np.array([0, 1, 77, 4095, 8000, 8190, 8191])
+    qr = bf16_stored(oracle.rope(np64(q), pos, base))
+    ro, rl = oracle.prefill_rows(qr, krr, np64(v), 1 / math.sqrt(D), True,
+                                 np.tile(rows, (Hq, 1)))
+    go = np64(o)[:, :, rows]
+    eo = np.abs(go - ro).max()
+    el = np.abs(lse.cpu().numpy()[:, :, rows] - rl).max()
+    say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= 2e-2 and el <= LSE_TOL
+
+
+def test_kv_append_rope_stores_rotated_keys():
+    B, Hkv, cap, D, base = 3, 2, 5000, 128, 10000.0
+    say(f"[append rope] B={B} cap={cap}")
+    rng = np.random.default_rng(8)
+    kc = torch.zeros(B, Hkv, cap, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kn = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float32)).to(torch.bfloat16)
+    vn = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float32)).to(torch.bfloat16)
+    lens = np.array([0, 1, 4999], dtype=np.int32)
+    sl = torch.from_numpy(lens.copy()).to(DEV)
+    attn.attn_kv_append(kn.to(DEV), vn.to(DEV), kc, vc, sl, rope_base=base)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        ref = bf16_stored(oracle.rope(np64(kn)[b], L, base))
+        got = np64(kc)[b, :, L]
+        assert np.abs(got - ref).max() <= 2 ** -8 * np.abs(ref).max()
+        assert torch.equal(vc[b, :, L].cpu(), vn[b])
+    assert sl.cpu().tolist() == [1, 2, 5000]
