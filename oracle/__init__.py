@@ -39,6 +39,7 @@ invariants, planted mistakes).  No function here is "parity unpinned".
 from .attention import (  # noqa: F401
     prefill,
     prefill_rows,
+    prefill_varlen,
     decode,
     lse_combine,
     softmax_probabilities,

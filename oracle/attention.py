@@ -137,6 +137,41 @@ def prefill_rows(q, k, v, scale, causal, rows):
     return o, lse
 
 
+def prefill_varlen(q, k, v, cu_seqlens, Hq, Hkv, scale, causal):
+    """Prefill of a ragged batch: each sequence is attended on its own.
+
+    Sequence b has S_b = cu[b+1] - cu[b] tokens; q (and the returned o) is a
+    flat array of [Hq, S_b, D] blocks at element offset Hq*D*cu[b], k and v of
+    [Hkv, S_b, D] blocks at Hkv*D*cu[b] (the packed layout of the decode
+    cache, with the query rows packed the same way).  The returned lse holds
+    [Hq, S_b] blocks at offset Hq*cu[b].  Padding never enters a score: this
+    is the padding mask of "Attention三算子融合实战" 4.3 written as separate
+    sequences.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    q, k, v = _f64(q).reshape(-1), _f64(k).reshape(-1), _f64(v).reshape(-1)
+    B = len(cu) - 1
+    N = int(cu[-1])
+    if N and q.size % (Hq * N):
+        raise ValueError("q does not match cu_seqlens")
+    D = q.size // (Hq * N) if N else 0
+    if k.size != Hkv * N * D or v.size != k.size:
+        raise ValueError("k, v do not match cu_seqlens")
+    o = np.zeros(Hq * N * D)
+    lse = np.zeros(Hq * N)
+    for b in range(B):
+        S = int(cu[b + 1] - cu[b])
+        if S <= 0:
+            continue
+        qb = q[Hq * D * cu[b]: Hq * D * cu[b + 1]].reshape(1, Hq, S, D)
+        kb = k[Hkv * D * cu[b]: Hkv * D * cu[b + 1]].reshape(1, Hkv, S, D)
+        vb = v[Hkv * D * cu[b]: Hkv * D * cu[b + 1]].reshape(1, Hkv, S, D)
+        ob, lb = prefill(qb, kb, vb, scale, causal)
+        o[Hq * D * cu[b]: Hq * D * cu[b + 1]] = ob.reshape(-1)
+        lse[Hq * cu[b]: Hq * cu[b + 1]] = lb.reshape(-1)
+    return o, lse
+
+
 def decode(q, kcache, vcache, seqlens, scale, Hkv):
     """Decode attention: one query row per sequence against its whole cache.
 

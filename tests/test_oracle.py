@@ -373,3 +373,65 @@ def test_planted_mistake_is_caught(monkeypatch, mutation):
             return P, lse
         monkeypatch.setattr(A, "_two_pass_softmax", bad)
     assert not _pins_hold(), f"planted mistake {mutation} not caught"
+
+
+# ------------------------------------------------------- ragged batch prefill
+
+def _pack(blocks):
+    return np.concatenate([b.reshape(-1) for b in blocks]) if blocks else \
+        np.zeros(0)
+
+
+def test_varlen_equal_lengths_equals_the_dense_batch():
+    # all S_b equal: the packed layout of [B, H, S, D] is the dense layout
+    B, Hq, Hkv, S, D = 3, 4, 2, 9, 8
+    q, k, v = prefill_np(B, Hq, Hkv, S, D, seed=21)
+    cu = np.arange(B + 1) * S
+    o, lse = oracle.prefill_varlen(q, k, v, cu, Hq, Hkv, 0.3, True)
+    ro, rl = oracle.prefill(q, k, v, 0.3, True)
+    assert np.abs(o - ro.reshape(-1)).max() < TOL
+    assert np.abs(lse - rl.reshape(-1)).max() < TOL
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    # each block equals the prefill of that sequence alone, and changing
+    # one sequence's values leaves the others' results unchanged
+    Hq, Hkv, D = 2, 1, 8
+    lens = [5, 0, 1, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    rng = np.random.default_rng(22)
+    qs = [rng.standard_normal((Hq, L, D)) for L in lens]
+    ks = [rng.standard_normal((Hkv, L, D)) for L in lens]
+    vs = [rng.standard_normal((Hkv, L, D)) for L in lens]
+    o, lse = oracle.prefill_varlen(_pack(qs), _pack(ks), _pack(vs), cu, Hq,
+                                   Hkv, 0.5, True)
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        ro, rl = oracle.prefill(qs[b][None], ks[b][None], vs[b][None], 0.5,
+                                True)
+        assert np.abs(o[Hq * D * cu[b]: Hq * D * cu[b + 1]] -
+                      ro.reshape(-1)).max() < TOL
+        assert np.abs(lse[Hq * cu[b]: Hq * cu[b + 1]] - rl.reshape(-1)).max() \
+            < TOL
+    ks2 = [x.copy() for x in ks]
+    ks2[3] = ks2[3] * 5.0
+    o2, _ = oracle.prefill_varlen(_pack(qs), _pack(ks2), _pack(vs), cu, Hq,
+                                  Hkv, 0.5, True)
+    keep = slice(0, Hq * D * cu[3])
+    assert np.abs(o2[keep] - o[keep]).max() == 0.0
+
+
+def test_varlen_causal_first_row_is_v0_of_its_own_sequence():
+    # the first token of every sequence sees only itself: o = its own v0
+    Hq, Hkv, D = 1, 1, 4
+    lens = [3, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal(sum(lens) * D)
+    k = rng.standard_normal(sum(lens) * D)
+    v = rng.standard_normal(sum(lens) * D)
+    o, _ = oracle.prefill_varlen(q, k, v, cu, Hq, Hkv, 1.0, True)
+    for b in range(2):
+        r = cu[b] * D
+        assert np.abs(o[r: r + D] - v[r: r + D]).max() < TOL
