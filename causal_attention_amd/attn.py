@@ -66,6 +66,9 @@ def lib():
         L.attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
                                         i, f, i, f, vp]
         L.attn_prefill_rope.restype = i
+        L.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                          i, f, i, vp]
+        L.attn_prefill_varlen.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -235,6 +238,50 @@ def attn_prefill_rope(q, k, v, rope_base, causal=True, scale=None, out=None,
     if st != 0:
         raise AttnError(st, "attn_prefill_rope")
     return out, lse, k_rot
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
+                        causal=True, scale=None, out=None, lse=None,
+                        with_lse=True):
+    """Prefill of a ragged batch (bf16), each sequence attended on its own.
+
+    cu_seqlens int32 [B+1] on the GPU (cu[0] = 0, S_b = cu[b+1] - cu[b]);
+    q (and o) hold [Hq, S_b, D] blocks at element offset Hq*D*cu[b], k and v
+    [Hkv, S_b, D] blocks at Hkv*D*cu[b] (any contiguous shape with that many
+    elements); lse [Hq*cu[B]] holds [Hq, S_b] blocks at offset Hq*cu[b].
+    ``max_seqlen`` bounds every S_b.  Returns (o, lse).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, None)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    B = cu_seqlens.shape[0] - 1
+    if B < 0:
+        raise ValueError("cu_seqlens needs B + 1 entries")
+    if q.numel() % (Hq * D) or k.numel() % (Hkv * D) or \
+            q.numel() // (Hq * D) != k.numel() // (Hkv * D) or \
+            v.numel() != k.numel():
+        raise ValueError("q, k, v sizes do not match Hq, Hkv and D")
+    N = q.numel() // (Hq * D)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, None)
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's size")
+    if with_lse and lse is None:
+        lse = torch.empty(Hq * N, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, None)
+        if lse.numel() != Hq * N:
+            raise ValueError("lse must have Hq * cu[B] entries")
+    st = lib().attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                   _ptr(lse), _ptr(cu_seqlens), B,
+                                   int(max_seqlen), Hq, Hkv, D, float(scale),
+                                   int(bool(causal)), _stream())
+    if st != 0:
+        raise AttnError(st, "attn_prefill_varlen")
+    return out, lse
 
 
 def attn_kv_append(k_new, v_new, kcache, vcache, seqlens, rope_base=0.0):

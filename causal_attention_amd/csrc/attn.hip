@@ -75,7 +75,8 @@ template <typename T, template <int, bool> class Launcher>
 int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
                    int B, int Hq, int Hkv, int S, int D, float scale,
                    int causal, void* stream, int use_rope = 0,
-                   const attn::RopeRates& rope = attn::RopeRates{}) {
+                   const attn::RopeRates& rope = attn::RopeRates{},
+                   const int* cu_seqlens = nullptr) {
   const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
   const dim3 grid((unsigned)(B * Hq * n_qtiles));
   const dim3 block(kPrefillThreads);
@@ -85,17 +86,21 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   if (D == 64) {
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
-                              sl2, n_qtiles, ncu, use_rope, rope);
+                              sl2, n_qtiles, ncu, use_rope, rope,
+                              cu_seqlens);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles, ncu, use_rope, rope);
+                               S, sl2, n_qtiles, ncu, use_rope, rope,
+                              cu_seqlens);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                               S, sl2, n_qtiles, ncu, use_rope, rope);
+                               S, sl2, n_qtiles, ncu, use_rope, rope,
+                              cu_seqlens);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
-                                S, sl2, n_qtiles, ncu, use_rope, rope);
+                                S, sl2, n_qtiles, ncu, use_rope, rope,
+                              cu_seqlens);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -108,10 +113,10 @@ struct Half16Prefill {
     static void run(dim3 g, dim3 b, hipStream_t st, const T* q, const T* k,
                     const T* v, T* o, float* lse, int B, int Hq, int Hkv,
                     int S, float sl2, int nq, int ncu, int use_rope,
-                    const attn::RopeRates& rope) {
+                    const attn::RopeRates& rope, const int* cu_seqlens) {
       hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st,
                          q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu,
-                         use_rope, rope);
+                         use_rope, rope, cu_seqlens);
     }
   };
 };
@@ -121,7 +126,8 @@ struct F32Prefill {
   static void run(dim3 g, dim3 b, hipStream_t st, const float* q,
                   const float* k, const float* v, float* o, float* lse, int B,
                   int Hq, int Hkv, int S, float sl2, int nq, int ncu,
-                  int /*use_rope*/, const attn::RopeRates& /*rope*/) {
+                  int /*use_rope*/, const attn::RopeRates& /*rope*/,
+                  const int* /*cu_seqlens*/) {
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
                        k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
@@ -322,6 +328,22 @@ int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
       static_cast<const __bf16*>(q), kr, static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), lse, B, Hq, Hkv, S, D, scale, causal, stream,
       1, rope);
+}
+
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const int* cu_seqlens, int B,
+                        int max_seqlen, int Hq, int Hkv, int D, float scale,
+                        int causal, void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, max_seqlen, D,
+                               scale, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!cu_seqlens) return ATTN_ERR_NULL;
+  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
+  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
+      max_seqlen, D, scale, causal, stream, 0, attn::RopeRates{}, cu_seqlens);
 }
 
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,

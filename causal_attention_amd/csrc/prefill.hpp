@@ -186,8 +186,9 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ LSE, int B, int Hq, int Hkv, int S, float scale_log2,
-    int n_qtiles, int n_cu, int use_rope, RopeRates rope) {
+    float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
+    float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
+    const int* __restrict__ cu_seqlens) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -207,9 +208,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const TileCoord tc =
       tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
-  const T* Qp = Q + (size_t)(tc.b * Hq + tc.hq) * S * D;
-  const T* Kp = K + (size_t)(tc.b * Hkv + tc.g) * S * D;
-  const T* Vp = V + (size_t)(tc.b * Hkv + tc.g) * S * D;
+  // Length of this sequence and the first row of (batch, head) in Q / O /
+  // LSE and in K / V: dense [B, H, S, D], or a ragged batch (cu_seqlens:
+  // sequence b is a [H, S_b, D] block at row offset H * cu[b]).
+  int S = S_all;
+  size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
+  size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
+  if (cu_seqlens != nullptr) {
+    const int c0 = cu_seqlens[tc.b];
+    S = cu_seqlens[tc.b + 1] - c0;
+    if (tc.qt * kPrefillBM >= S) return;   // query tile past this sequence
+    q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
+    kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
+  }
+  const T* Qp = Q + q_row0 * D;
+  const T* Kp = K + kv_row0 * D;
+  const T* Vp = V + kv_row0 * D;
 
   const int q_lo = tc.qt * BM;
   const int q_hi = min(S, q_lo + BM);
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   const float l_tot = l_i + swap_halves(l_i);
   if (query < S) {
     const float inv = 1.f / l_tot;
-    T* orow = O + (size_t)(tc.b * Hq + tc.hq) * S * D + (size_t)query * D;
+    T* orow = O + (q_row0 + query) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hh) = pr;
       }
     if (LSE != nullptr && hh == 0)
-      LSE[(size_t)(tc.b * Hq + tc.hq) * S + query] =
+      LSE[q_row0 + query] =
           (m_i + fast_log2(l_tot)) * kLn2;
   }
 }

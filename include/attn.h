@@ -109,6 +109,27 @@ int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
                       void* stream);
 
 /*
+ * Prefill attention over a ragged batch (variable sequence lengths), bf16:
+ * the padding mask of the attention-fusion page, section 4.3, and the
+ * dynamic shapes of its section 6.1, with no padding stored at all.
+ *   cu_seqlens: DEVICE int32 [B + 1], non-decreasing, cu[0] = 0: sequence b
+ *               has S_b = cu[b+1] - cu[b] tokens.
+ *   q, o      : sequence b is a [Hq, S_b, D] bf16 block at element offset
+ *               Hq * D * cu[b]        (the packed layout of attn_decode's
+ *   k, v      : [Hkv, S_b, D] blocks at Hkv * D * cu[b]   caches)
+ *   lse       : [Hq, S_b] fp32 blocks at offset Hq * cu[b], or NULL.
+ *   max_seqlen: an upper bound of every S_b, known on the host; it sizes the
+ *               grid (rows past it are not computed).
+ * Each sequence is attended on its own (causal or full), exactly as
+ * attn_prefill with B = 1 and S = S_b.  Other arguments and errors as
+ * attn_prefill (with S = max_seqlen); cu_seqlens NULL: ATTN_ERR_NULL.
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const int* cu_seqlens, int B,
+                        int max_seqlen, int Hq, int Hkv, int D, float scale,
+                        int causal, void* stream);
+
+/*
  * Prefill attention, fp32 storage.  Same arguments and layouts as
  * attn_prefill with every tensor fp32.  The probabilities P stay fp32 (the
  * accuracy setting of the attention-fusion page, sections 3.3 and 5.5).

@@ -549,3 +549,50 @@ def test_kv_append_rope_stores_rotated_keys():
         assert np.abs(got - ref).max() <= 2 ** -8 * np.abs(ref).max()
         assert torch.equal(vc[b, :, L].cpu(), vn[b])
     assert sl.cpu().tolist() == [1, 2, 5000]
+
+
+# ------------------------------------------------------- ragged batch prefill
+
+def packed_inputs(lens, Hq, Hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    N = int(np.sum(lens))
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    q = bf(rng.standard_normal(Hq * N * D))
+    k = bf(rng.standard_normal(Hkv * N * D))
+    v = bf(rng.standard_normal(Hkv * N * D))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, cu
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (1, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_varlen_matches_oracle(D, Hq, Hkv, causal):
+    lens = [0, 1, 127, 128, 129, 1000, 257]
+    say(f"[prefill varlen] lens={lens} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    q, k, v, cu = packed_inputs(lens, Hq, Hkv, D, 31)
+    o, lse = attn.attn_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV),
+                                      torch.from_numpy(cu).to(DEV),
+                                      max(lens), Hq, Hkv, D, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_varlen(np64(q), np64(k), np64(v), cu, Hq, Hkv,
+                                   1 / math.sqrt(D), causal)
+    eo, el = np.abs(np64(o) - ro).max(), np.abs(lse.cpu().numpy() - rl).max()
+    say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= 2e-2 and el <= LSE_TOL
+
+
+def test_prefill_varlen_equal_lengths_is_the_dense_kernel():
+    # with equal lengths the packed layout is [B, H, S, D]; every workgroup
+    # does the same arithmetic as the dense launch, so the results match
+    # bit for bit
+    B, Hq, Hkv, S, D = 3, 8, 2, 300, 128
+    say(f"[prefill varlen == dense] B={B} S={S}")
+    q, k, v = (t.to(DEV) for t in inputs.prefill_inputs(B, Hq, Hkv, S, D,
+                                                         "bf16", 1.0, 3))
+    cu = torch.arange(B + 1, dtype=torch.int32, device=DEV) * S
+    o, lse = attn.attn_prefill_varlen(q, k, v, cu, S, Hq, Hkv, D)
+    do, dl = attn.attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(B, Hq, S, D), do)
+    assert torch.equal(lse.view(B, Hq, S), dl)
