@@ -14,7 +14,9 @@ average duration measured with HIP events; the decode's KV-cache GB/s
 (K and V bytes read once per KV head, plus q and o) is in ``decode``.  Both
 carry a ``roofline`` object against MI355X's published peaks (2.5 PFLOP/s
 dense bf16 MFMA, 8 TB/s HBM3E).  ``cpu_baseline`` times the fp64 CPU oracle
-on the host on a bounded sample of the same workload.
+on the host on a bounded sample of the same workload.  With ``--extras`` the
+line also carries ``extras``: the widened paths (fp16 storage, RoPE, ragged
+batch) timed on the same shapes.
 """
 
 import argparse
@@ -135,6 +137,92 @@ def cpu_baseline(wp, wd):
     }
 
 
+def extras(attn, inputs, torch, dev, wp, wd, reps=20):
+    """The widened paths on the same shapes, each timed with HIP events over
+    ``reps`` back-to-back launches on warm inputs (they fit the last-level
+    cache): fp16 storage, RoPE, the ragged batch.  Rates are algorithmic
+    (the same FLOP and byte counts as the main line) against the same
+    peaks (fp16 dense MFMA peak = bf16's)."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps          # ms
+
+    def tf(flops, ms):
+        t = flops / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 3), "TFLOP/s": round(t, 1),
+                "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+
+    def gb(nbytes, ms):
+        g = nbytes / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 3), "GB/s": round(g, 1),
+                "frac": round(g / PEAK_HBM_GBS, 4)}
+
+    out = {}
+    flops = prefill_flops(wp.B, wp.Hq, wp.S, wp.D)
+    q, k, v = (t.to(dev) for t in inputs.prefill_inputs(
+        wp.B, wp.Hq, wp.Hkv, wp.S, wp.D, "f16", wp.sigma, wp.seed))
+    o = torch.empty_like(q)
+    call = attn.prepare_prefill(q, k, v, o, None, causal=True)
+    out["prefill_f16"] = tf(flops, timed(call))
+    sl, dq, kc, vc = inputs.decode_inputs(wd.B, wd.Hq, wd.Hkv, wd.D,
+                                          lmin=wd.lmin, lmax=wd.lmax,
+                                          dtype="f16", sigma=wd.sigma,
+                                          seed=wd.seed)
+    dq, kc, vc = dq.to(dev), kc.to(dev), vc.to(dev)
+    sld = torch.from_numpy(sl).to(dev)
+    ws = attn.new_decode_workspace(wd.B, wd.Hq, wd.Hkv, wd.D, 0, dev)
+    do = torch.empty_like(dq)
+    dcall = attn.prepare_decode(dq, kc, vc, sld, do, wd.Hkv, ws)
+    dbytes = decode_bytes(sl, wd.Hq, wd.Hkv, wd.D)
+    out["decode_f16"] = gb(dbytes, timed(dcall))
+
+    # RoPE: prefill with q rotated on load plus the K rotation pass (timed
+    # together; the FLOP count is the attention's), and decode over a padded
+    # cache with q rotated in the kernel
+    qb, kb, vb = (t.to(dev) for t in inputs.prefill_inputs(
+        wp.B, wp.Hq, wp.Hkv, wp.S, wp.D, "bf16", wp.sigma, wp.seed))
+    ob, kr = torch.empty_like(qb), torch.empty_like(kb)
+    out["prefill_rope"] = tf(flops, timed(
+        lambda: attn.attn_prefill_rope(qb, kb, vb, 10000.0, out=ob,
+                                       with_lse=False, k_rot=kr)))
+    cap = wd.lmax
+    kp = torch.zeros(wd.B, wd.Hkv, cap, wd.D, dtype=torch.bfloat16,
+                     device=dev)
+    vp = torch.zeros_like(kp)
+    dqb = dq.to(torch.bfloat16)
+    dob = torch.empty_like(dqb)
+    out["decode_padded_rope"] = gb(dbytes, timed(
+        lambda: attn.attn_decode_padded(dqb, kp, vp, sld, out=dob,
+                                        workspace=ws, rope_base=10000.0)))
+
+    # ragged batch: B sequences with the decode workload's lengths
+    lens = sl.astype("int64")
+    N = int(lens.sum())
+    g = torch.Generator().manual_seed(1)
+    qv = torch.randn(wp.Hq * N * wp.D, generator=g).to(torch.bfloat16).to(dev)
+    kv = torch.randn(wp.Hkv * N * wp.D, generator=g).to(torch.bfloat16).to(dev)
+    vv = torch.randn(wp.Hkv * N * wp.D, generator=g).to(torch.bfloat16).to(dev)
+    cu = torch.tensor([0] + list(lens.cumsum()), dtype=torch.int32,
+                      device=dev)
+    ov = torch.empty_like(qv)
+    vflops = sum(4 * wp.D * wp.Hq * int(L) * (int(L) + 1) // 2 for L in lens)
+    out["prefill_varlen"] = tf(vflops, timed(
+        lambda: attn.attn_prefill_varlen(qv, kv, vv, cu, int(lens.max()),
+                                         wp.Hq, wp.Hkv, wp.D, out=ov,
+                                         with_lse=False)))
+    out["prefill_varlen"]["sequences"] = f"{len(lens)} lengths of the decode workload, sum {N}"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +237,11 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     metavar="MB", help="only run a plain MB-sized device copy "
                     "(to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the fp16 / RoPE / ragged-batch paths "
+                    "(reported under \"extras\"; off by default so the "
+                    "kernel statistics of the default run hold only the "
+                    "main step's launches)")
     args = ap.parse_args()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
@@ -321,6 +414,8 @@ def main():
             },
         },
     }
+    if args.extras:
+        out["extras"] = extras(attn, inputs, torch, dev, wp, wd)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp, wd)
     print(json.dumps(out), flush=True)
