@@ -17,27 +17,29 @@
 // every CU from the first microsecond to the last:
 //  * Work split ("stream-K"): the caches are cut into 32-key blocks and the
 //    blocks of all (sequence, KV head) segments, in that order, are divided
-//    into P equal contiguous ranges, one per workgroup (P = the CU count by
-//    default).  Every workgroup gets the same number of blocks whatever the
-//    length mix, and all of them start together.  A segment that lies wholly
-//    in one range is finished by its workgroup; a segment cut by range
-//    boundaries leaves one partial (normalised output and LSE) per piece for
-//    the combine kernel.
-//  * Inside a workgroup each wave takes every 4th block of the current
-//    segment and streams it through a private double-buffered LDS ring:
-//    K, V and the segment's G query rows arrive by gfx950's direct loads
-//    (global_load_lds_dwordx4, 1 KB contiguous per instruction), the next
-//    block's loads are issued before the current one is multiplied, and no
-//    barrier is needed until the segment ends.
+//    into P equal contiguous ranges, one per single-wave workgroup (P = two
+//    per CU by default).  Every workgroup gets the same number of blocks
+//    whatever the length mix, and all of them start together.  A segment
+//    that lies wholly in one range is finished by its workgroup; a segment
+//    cut by range boundaries leaves one partial (normalised output and LSE)
+//    per piece, and the range holding its first block records which ranges
+//    hold the others, for the combine kernel.
+//  * Each wave streams its blocks in order through a double-buffered LDS
+//    ring: K, V and the segment's G query rows arrive by gfx950's direct
+//    loads (global_load_lds_dwordx4, 1 KB contiguous per instruction), and
+//    the next block's loads (across segment ends too) are issued before the
+//    current one is multiplied.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (_f16 for
-//    fp16 inputs; the heads
-//    are MFMA columns, the other columns are zero): the A operand K comes from
-//    LDS rows, V^T from transposed LDS reads (ds_read_b64_tr_b16), and the
-//    probabilities stay in registers as the B operand of the second product.
-//    The running output is rescaled only when the row max grows by more than
-//    2^8 (exact: the final division by l cancels any common reference).
-//  * At a segment end the waves merge (m, l, O) through LDS (each wave's free
-//    ring buffer) and one pass writes the final output or the partial.
+//    fp16 inputs; the heads are MFMA columns, the other columns are zero):
+//    K rows are the A operand, V^T comes from transposed LDS reads
+//    (ds_read_b64_tr_b16), the query rows are read once per piece (and
+//    rotated there when RoPE is on), and the probabilities stay in registers
+//    as the B operand of the second product.  The running output is rescaled
+//    only when the row max grows by more than 2^8 (exact: the final division
+//    by l cancels any common reference).
+//  * The caches are either packed per sequence or padded to a per-sequence
+//    capacity (the serving-loop layout of attn_kv_append); only the address
+//    of a segment's first row differs.
 #pragma once
 
 #include "common.hpp"
