@@ -1,6 +1,6 @@
-// Decode kernels: one query row per sequence against its packed KV cache,
-// split over the keys of the whole batch, then a log-sum-exp combine of the
-// pieces of each (sequence, query head) that were split.
+// Decode kernels: one query row per sequence against its KV cache (packed or
+// padded), split over the keys of the whole batch, then a log-sum-exp combine
+// of the pieces of each (sequence, query head) that were split.
 //
 // Method ("Attention三算子融合实战：从Triton到CUDA的推理加速优化"): the decode
 // setting of section 1.3 (one query row, K and V as long as the history), the
