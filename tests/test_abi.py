@@ -23,7 +23,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["attn_prefill", "attn_prefill_f32", "attn_decode",
+    for n in ["attn_prefill", "attn_prefill_f16", "attn_prefill_f32",
+              "attn_prefill_rope", "attn_prefill_varlen", "attn_decode",
+              "attn_decode_f16", "attn_decode_padded", "attn_kv_append",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
               "attn_status_string"]:
         assert n in names
@@ -48,7 +50,8 @@ def prefill(fn="attn_prefill", q=A, k=A, v=A, o=A, lse=A, B=1, Hq=8, Hkv=2,
                           None)
 
 
-@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f32"])
+@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f16",
+                                "attn_prefill_f32"])
 def test_prefill_argument_errors(fn):
     assert prefill(fn, B=-1) == -2
     assert prefill(fn, S=-5) == -2
@@ -69,7 +72,8 @@ def test_prefill_argument_errors(fn):
     assert prefill(fn, B=65536, Hq=1024, Hkv=1, S=1 << 20) == -2
 
 
-@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f32"])
+@pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f16",
+                                "attn_prefill_f32"])
 def test_prefill_empty_is_a_noop(fn):
     # B == 0 or S == 0: nothing to do, even with NULL pointers
     assert prefill(fn, q=None, k=None, v=None, o=None, lse=None, B=0) == 0
@@ -77,13 +81,102 @@ def test_prefill_empty_is_a_noop(fn):
 
 
 def decode(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, scale=0.1,
-           ns=0, lse=None, ws=A, wsb=1 << 30):
+           ns=0, lse=None, ws=A, wsb=1 << 30, fn="attn_decode"):
     L = attn.lib()
-    return L.attn_decode(q, kc, vc, sl, o, B, Hq, Hkv, D, scale, ns, lse, ws,
-                         wsb, None)
+    return getattr(L, fn)(q, kc, vc, sl, o, B, Hq, Hkv, D, scale, ns, lse, ws,
+                          wsb, None)
 
 
-def test_decode_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_decode", "attn_decode_f16"])
+def test_decode_argument_errors(fn):
+    import functools
+    decode_ = functools.partial(decode, fn=fn)
+    assert decode_(B=-1) == -2
+    assert decode_(Hq=8, Hkv=3) == -3
+    assert decode_(D=80) == -4
+    assert decode_(ns=-1) == -7
+    assert decode_(q=None) == -1
+    assert decode_(sl=A + 2) == -5
+    assert decode_(wsb=100) == -6
+    assert decode_(scale=float("nan")) == -9
+
+
+def padded(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, cap=64,
+           scale=0.1, ns=0, lse=None, rope=0.0, ws=A, wsb=1 << 30):
+    return attn.lib().attn_decode_padded(q, kc, vc, sl, o, B, Hq, Hkv, D, cap,
+                                         scale, ns, lse, rope, ws, wsb, None)
+
+
+def test_decode_padded_argument_errors():
+    assert padded(cap=0) == -2
+    assert padded(cap=-3) == -2
+    assert padded(B=0, cap=0) == 0
+    assert padded(Hq=8, Hkv=3) == -3
+    assert padded(D=96) == -4
+    assert padded(q=None) == -1
+    assert padded(kc=A + 8) == -5
+    assert padded(wsb=10) == -6
+    assert padded(rope=-1.0) == -9
+    assert padded(rope=float("inf")) == -9
+
+
+def append(kn=A, vn=A, kc=A, vc=A, sl=A, B=4, Hkv=2, D=128, cap=64, rope=0.0):
+    return attn.lib().attn_kv_append(kn, vn, kc, vc, sl, B, Hkv, D, cap, rope,
+                                     None)
+
+
+def test_kv_append_argument_errors():
+    assert append(B=-1) == -2
+    assert append(cap=-1) == -2
+    assert append(cap=0) == -2
+    assert append(Hkv=0) == -3
+    assert append(D=96) == -4
+    assert append(kn=None) == -1
+    assert append(sl=None) == -1
+    assert append(vc=A + 8) == -5
+    assert append(sl=A + 2) == -5
+    assert append(rope=float("nan")) == -9
+    assert append(rope=-2.0) == -9
+    assert append(B=0, kn=None, vn=None, kc=None, vc=None, sl=None) == 0
+
+
+def prefill_rope(q=A, k=A, v=A, o=A, lse=A, kr=A, B=1, Hq=8, Hkv=2, S=64,
+                 D=128, scale=0.1, causal=1, rope=10000.0):
+    return attn.lib().attn_prefill_rope(q, k, v, o, lse, kr, B, Hq, Hkv, S, D,
+                                        scale, causal, rope, None)
+
+
+def test_prefill_rope_argument_errors():
+    assert prefill_rope(kr=None) == -1
+    assert prefill_rope(kr=A + 8) == -5
+    assert prefill_rope(rope=0.0) == -9
+    assert prefill_rope(rope=-1.0) == -9
+    assert prefill_rope(rope=float("nan")) == -9
+    assert prefill_rope(scale=0.0) == -9
+    assert prefill_rope(D=80) == -4
+    assert prefill_rope(Hq=8, Hkv=3) == -3
+    assert prefill_rope(B=0, q=None, k=None, v=None, o=None, kr=None) == 0
+
+
+def varlen(q=A, k=A, v=A, o=A, lse=A, cu=A, B=3, maxs=100, Hq=8, Hkv=2,
+           D=128, scale=0.1, causal=1):
+    return attn.lib().attn_prefill_varlen(q, k, v, o, lse, cu, B, maxs, Hq,
+                                          Hkv, D, scale, causal, None)
+
+
+def test_prefill_varlen_argument_errors():
+    assert varlen(cu=None) == -1
+    assert varlen(cu=A + 2) == -5
+    assert varlen(q=None) == -1
+    assert varlen(maxs=-1) == -2
+    assert varlen(D=96) == -4
+    assert varlen(Hq=8, Hkv=3) == -3
+    assert varlen(scale=float("nan")) == -9
+    assert varlen(B=0, q=None, k=None, v=None, o=None, cu=None) == 0
+    assert varlen(maxs=0, q=None, k=None, v=None, o=None, cu=None) == 0
+
+
+def test_decode_argument_errors_detail():
     assert decode(B=-1) == -2
     assert decode(Hq=8, Hkv=3) == -3
     assert decode(Hq=12, Hkv=1) == -3      # group size 12 not compiled
