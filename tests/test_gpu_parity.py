@@ -483,6 +483,50 @@ def test_decode_step_graph_replay(rope_base):
         assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
 
 
+def test_prefill_graph_replay():
+    """A prefill launch captured once in a graph and replayed with new
+    inputs copied in between: every replay equals an eager launch on the
+    same inputs bit for bit and matches the oracle."""
+    B, Hq, Hkv, S, D = 2, 8, 2, 300, 128
+    say(f"[graph prefill] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    q = torch.empty(B, Hq, S, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(B, Hkv, S, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device=DEV)
+
+    def load(seed):
+        for dst, src in zip((q, k, v), inputs.prefill_inputs(
+                B, Hq, Hkv, S, D, "bf16", 1.0, seed)):
+            dst.copy_(src.to(DEV))
+
+    load(20)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        attn.attn_prefill(q, k, v, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attn.attn_prefill(q, k, v, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for t in range(3):
+        load(21 + t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eo, el = attn.attn_prefill(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, eo) and torch.equal(lse, el)
+        ro, rl = oracle.prefill(np64(q), np64(k), np64(v), 1 / math.sqrt(D),
+                                True)
+        err = np.abs(np64(o) - ro).max()
+        say(f"   replay {t}: max|dO|={err:.3e}")
+        assert err <= o_tol("bf16")
+        assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
+
+
 # ------------------------------------------------------------------- RoPE
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,D", [(1, 8, 2, 300, 128),
