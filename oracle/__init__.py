@@ -40,6 +40,7 @@ from .attention import (  # noqa: F401
     prefill,
     prefill_rows,
     prefill_varlen,
+    prefill_padded,
     decode,
     lse_combine,
     softmax_probabilities,

@@ -172,6 +172,31 @@ def prefill_varlen(q, k, v, cu_seqlens, Hq, Hkv, scale, causal):
     return o, lse
 
 
+def prefill_padded(q, k, v, seqlens, scale, causal):
+    """Prefill of a padded batch: q [B,Hq,S,D], k, v [B,Hkv,S,D], sequence b
+    valid in its first L_b = clamp(seqlens[b], 0, S) rows.
+
+    Valid rows attend the valid keys only (the padding mask of
+    "Attention三算子融合实战" 4.3: keys past the valid length are -inf), i.e.
+    sequence b is attended as the dense prefill of its first L_b rows; the
+    padding rows get o = 0 and lse = -inf (the empty-row reading also used
+    by decode for an empty cache).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, S, D = q.shape
+    o = np.zeros((B, Hq, S, D))
+    lse = np.full((B, Hq, S), -np.inf)
+    for b in range(B):
+        L = min(max(int(seqlens[b]), 0), S)
+        if L == 0:
+            continue
+        ob, lb = prefill(q[b:b + 1, :, :L], k[b:b + 1, :, :L],
+                         v[b:b + 1, :, :L], scale, causal)
+        o[b, :, :L] = ob[0]
+        lse[b, :, :L] = lb[0]
+    return o, lse
+
+
 def decode(q, kcache, vcache, seqlens, scale, Hkv):
     """Decode attention: one query row per sequence against its whole cache.
 

@@ -435,3 +435,47 @@ def test_varlen_causal_first_row_is_v0_of_its_own_sequence():
     for b in range(2):
         r = cu[b] * D
         assert np.abs(o[r: r + D] - v[r: r + D]).max() < TOL
+
+
+# ------------------------------------------------------------ padded batch
+
+def test_padded_full_lengths_equal_the_dense_batch():
+    B, Hq, Hkv, S, D = 2, 4, 2, 9, 8
+    q, k, v = prefill_np(B, Hq, Hkv, S, D, seed=24)
+    for causal in (True, False):
+        o, lse = oracle.prefill_padded(q, k, v, [S, S + 3], 0.3, causal)
+        ro, rl = oracle.prefill(q, k, v, 0.3, causal)
+        assert np.abs(o - ro).max() < TOL and np.abs(lse - rl).max() < TOL
+
+
+def test_padded_causal_rows_equal_dense_causal_rows():
+    # under the causal mask a valid row i < L never sees a key past i, so
+    # it already ignores the padding: the dense causal prefill of the whole
+    # padded tensors gives the same valid rows (no slicing involved)
+    B, Hq, Hkv, S, D = 3, 2, 1, 11, 8
+    q, k, v = prefill_np(B, Hq, Hkv, S, D, seed=25)
+    lens = [4, 11, 1]
+    o, lse = oracle.prefill_padded(q, k, v, lens, 0.4, True)
+    ro, rl = oracle.prefill(q, k, v, 0.4, True)
+    for b, L in enumerate(lens):
+        assert np.abs(o[b, :, :L] - ro[b, :, :L]).max() < TOL
+        assert np.abs(lse[b, :, :L] - rl[b, :, :L]).max() < TOL
+
+
+def test_padded_rows_and_content():
+    # padding rows are o = 0, lse = -inf; what the padding holds does not
+    # change any valid row (keys past L_b are masked even without causality)
+    B, Hq, Hkv, S, D = 3, 2, 2, 7, 4
+    q, k, v = prefill_np(B, Hq, Hkv, S, D, seed=26)
+    lens = [0, 3, 7]
+    for causal in (True, False):
+        o, lse = oracle.prefill_padded(q, k, v, lens, 0.5, causal)
+        q2, k2, v2 = (x.copy() for x in (q, k, v))
+        for b, L in enumerate(lens):
+            for t in (q2, k2, v2):
+                t[b, :, L:] = 1e3
+        o2, lse2 = oracle.prefill_padded(q2, k2, v2, lens, 0.5, causal)
+        for b, L in enumerate(lens):
+            assert (o[b, :, L:] == 0).all() and (lse[b, :, L:] == -np.inf).all()
+            assert np.array_equal(o2[b, :, :L], o[b, :, :L])
+            assert np.array_equal(lse2[b, :, :L], lse[b, :, :L])
