@@ -69,6 +69,9 @@ def lib():
         L.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
                                           i, f, i, vp]
         L.attn_prefill_varlen.restype = i
+        L.attn_prefill_padded.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                          i, f, i, vp]
+        L.attn_prefill_padded.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -281,6 +284,43 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
                                    int(bool(causal)), _stream())
     if st != 0:
         raise AttnError(st, "attn_prefill_varlen")
+    return out, lse
+
+
+def attn_prefill_padded(q, k, v, seqlens, causal=True, scale=None, out=None,
+                        lse=None, with_lse=True):
+    """Prefill of a padded batch (bf16): q [B,Hq,S,D], k, v [B,Hkv,S,D] as
+    for ``attn_prefill``, with seqlens int32 [B] on the GPU giving the valid
+    rows L_b of each sequence (clamped to [0, S]).  Rows i < L_b attend keys
+    j < L_b only; padding rows get o = 0 and lse = -inf.  Returns (o, lse).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    _check(seqlens, "seqlens", torch.int32, 1)
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if lse.shape != (B, Hq, S):
+            raise ValueError("lse must be [B,Hq,S]")
+    st = lib().attn_prefill_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                   _ptr(lse), _ptr(seqlens), B, Hq, Hkv, S, D,
+                                   float(scale), int(bool(causal)), _stream())
+    if st != 0:
+        raise AttnError(st, "attn_prefill_padded")
     return out, lse
 
 

@@ -76,7 +76,8 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
                    int B, int Hq, int Hkv, int S, int D, float scale,
                    int causal, void* stream, int use_rope = 0,
                    const attn::RopeRates& rope = attn::RopeRates{},
-                   const int* cu_seqlens = nullptr) {
+                   const int* cu_seqlens = nullptr,
+                   const int* seq_lens = nullptr) {
   const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
   const dim3 grid((unsigned)(B * Hq * n_qtiles));
   const dim3 block(kPrefillThreads);
@@ -87,20 +88,20 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
                               sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens);
+                              cu_seqlens, seq_lens);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens);
+                              cu_seqlens, seq_lens);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens);
+                              cu_seqlens, seq_lens);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                 S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens);
+                              cu_seqlens, seq_lens);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -113,10 +114,11 @@ struct Half16Prefill {
     static void run(dim3 g, dim3 b, hipStream_t st, const T* q, const T* k,
                     const T* v, T* o, float* lse, int B, int Hq, int Hkv,
                     int S, float sl2, int nq, int ncu, int use_rope,
-                    const attn::RopeRates& rope, const int* cu_seqlens) {
+                    const attn::RopeRates& rope, const int* cu_seqlens,
+                    const int* seq_lens) {
       hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st,
                          q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu,
-                         use_rope, rope, cu_seqlens);
+                         use_rope, rope, cu_seqlens, seq_lens);
     }
   };
 };
@@ -127,7 +129,7 @@ struct F32Prefill {
                   const float* k, const float* v, float* o, float* lse, int B,
                   int Hq, int Hkv, int S, float sl2, int nq, int ncu,
                   int /*use_rope*/, const attn::RopeRates& /*rope*/,
-                  const int* /*cu_seqlens*/) {
+                  const int* /*cu_seqlens*/, const int* /*seq_lens*/) {
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
                        k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
@@ -344,6 +346,22 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
       static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
       max_seqlen, D, scale, causal, stream, 0, attn::RopeRates{}, cu_seqlens);
+}
+
+int attn_prefill_padded(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const int* seqlens, int B, int Hq,
+                        int Hkv, int S, int D, float scale, int causal,
+                        void* stream) {
+  bool empty;
+  const int st =
+      check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!seqlens) return ATTN_ERR_NULL;
+  if (!aligned(seqlens, 4)) return ATTN_ERR_ALIGN;
+  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
+      S, D, scale, causal, stream, 0, attn::RopeRates{}, nullptr, seqlens);
 }
 
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,

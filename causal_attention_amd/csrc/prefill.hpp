@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
     float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
-    const int* __restrict__ cu_seqlens) {
+    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -209,8 +209,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   const TileCoord tc =
       tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
   // Length of this sequence and the first row of (batch, head) in Q / O /
-  // LSE and in K / V: dense [B, H, S, D], or a ragged batch (cu_seqlens:
-  // sequence b is a [H, S_b, D] block at row offset H * cu[b]).
+  // LSE and in K / V: dense [B, H, S, D]; or a ragged batch (cu_seqlens:
+  // sequence b is a [H, S_b, D] block at row offset H * cu[b]); or a dense
+  // batch padded to S_all (seq_lens: the first L_b rows of sequence b are
+  // valid; keys past L_b are masked, query rows past it get o = 0 and
+  // lse = -inf).
   int S = S_all;
   size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
   size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
@@ -220,6 +223,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     if (tc.qt * kPrefillBM >= S) return;   // query tile past this sequence
     q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
     kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
+  } else if (seq_lens != nullptr) {
+    S = min(max(seq_lens[tc.b], 0), S_all);
+  }
+  // Padding rows [S, S_all) of this query tile: o = 0, lse = -inf (a row of
+  // 32 lanes x two halves per wave, D/2 elements per lane).
+  auto pad_row = [&](int row) {
+    T* orow = O + (q_row0 + row) * D + hh * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{};
+    if (LSE != nullptr && hh == 0) LSE[q_row0 + row] = -INFINITY;
+  };
+  if (seq_lens != nullptr && tc.qt * kPrefillBM >= S) {
+    const int row = tc.qt * kPrefillBM + 32 * w + r;
+    if (row < S_all) pad_row(row);
+    return;                                 // whole tile is padding
   }
   const T* Qp = Q + q_row0 * D;
   const T* Kp = K + kv_row0 * D;
@@ -431,6 +450,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     if (LSE != nullptr && hh == 0)
       LSE[q_row0 + query] =
           (m_i + fast_log2(l_tot)) * kLn2;
+  } else if (seq_lens != nullptr && query < S_all) {
+    pad_row(query);
   }
 }
 

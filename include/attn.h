@@ -130,6 +130,24 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                         int causal, void* stream);
 
 /*
+ * Prefill attention over a padded batch, bf16: the padding mask of the
+ * attention-fusion page, section 4.3, on the dense layout of attn_prefill
+ * (every sequence stored with S rows, the first L_b of them valid).
+ *   q, o : [B, Hq, S, D] bf16   k, v : [B, Hkv, S, D] bf16
+ *   lse  : [B, Hq, S] fp32, or NULL.
+ *   seqlens: DEVICE int32 [B]; L_b = seqlens[b] clamped to [0, S].
+ * Rows i < L_b of sequence b attend keys j < L_b (and j <= i when causal),
+ * exactly as attn_prefill on the first L_b rows alone; the padding rows
+ * i >= L_b get o = 0 and lse = -inf.  Padding K / V rows are never read.
+ * Other arguments and errors as attn_prefill; seqlens NULL: ATTN_ERR_NULL,
+ * not 4-byte aligned: ATTN_ERR_ALIGN.
+ */
+int attn_prefill_padded(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const int* seqlens, int B, int Hq,
+                        int Hkv, int S, int D, float scale, int causal,
+                        void* stream);
+
+/*
  * Prefill attention, fp32 storage.  Same arguments and layouts as
  * attn_prefill with every tensor fp32.  The probabilities P stay fp32 (the
  * accuracy setting of the attention-fusion page, sections 3.3 and 5.5).

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["attn_prefill", "attn_prefill_f16", "attn_prefill_f32",
-              "attn_prefill_rope", "attn_prefill_varlen", "attn_decode",
+              "attn_prefill_rope", "attn_prefill_varlen",
+              "attn_prefill_padded", "attn_decode",
               "attn_decode_f16", "attn_decode_padded", "attn_kv_append",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
               "attn_status_string"]:
@@ -174,6 +175,25 @@ def test_prefill_varlen_argument_errors():
     assert varlen(scale=float("nan")) == -9
     assert varlen(B=0, q=None, k=None, v=None, o=None, cu=None) == 0
     assert varlen(maxs=0, q=None, k=None, v=None, o=None, cu=None) == 0
+
+
+def prefill_padded(q=A, k=A, v=A, o=A, lse=A, sl=A, B=3, Hq=8, Hkv=2, S=100,
+                   D=128, scale=0.1, causal=1):
+    return attn.lib().attn_prefill_padded(q, k, v, o, lse, sl, B, Hq, Hkv, S,
+                                          D, scale, causal, None)
+
+
+def test_prefill_padded_argument_errors():
+    assert prefill_padded(sl=None) == -1
+    assert prefill_padded(sl=A + 2) == -5
+    assert prefill_padded(q=None) == -1
+    assert prefill_padded(o=A + 8) == -5
+    assert prefill_padded(S=-1) == -2
+    assert prefill_padded(D=96) == -4
+    assert prefill_padded(Hq=8, Hkv=3) == -3
+    assert prefill_padded(scale=float("nan")) == -9
+    assert prefill_padded(B=0, q=None, k=None, v=None, o=None, sl=None) == 0
+    assert prefill_padded(S=0, q=None, k=None, v=None, o=None, sl=None) == 0
 
 
 def test_decode_argument_errors_detail():

@@ -527,6 +527,57 @@ def test_prefill_graph_replay():
         assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
 
 
+# ------------------------------------------------------------ padded batch
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,lens", [
+    (3, 8, 2, 300, 128, [0, 1, 300]),
+    (4, 8, 2, 257, 128, [129, 64, 200, 257]),
+    (4, 12, 12, 129, 64, [129, 65, 5, 128]),
+    (2, 8, 1, 1000, 128, [999, 333]),
+])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_padded_matches_oracle(B, Hq, Hkv, S, D, lens, causal):
+    say(f"[prefill padded] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} lens={lens} "
+        f"causal={causal}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 7)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = attn.attn_prefill_padded(q.to(DEV), k.to(DEV), v.to(DEV), sl,
+                                      causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_padded(np64(q), np64(k), np64(v), lens,
+                                   1 / math.sqrt(D), causal)
+    oo, ll = np64(o), lse.cpu().numpy()
+    for b, L in enumerate(lens):
+        assert (oo[b, :, L:] == 0).all() and (ll[b, :, L:] == -np.inf).all()
+        if L:
+            eo = np.abs(oo[b, :, :L] - ro[b, :, :L]).max()
+            el = np.abs(ll[b, :, :L] - rl[b, :, :L]).max()
+            say(f"   b={b} L={L} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+            assert eo <= o_tol("bf16") and el <= LSE_TOL
+
+
+def test_prefill_padded_full_lengths_equal_dense_and_ignore_padding():
+    # lengths = S: the dense kernel's results bit for bit; and values written
+    # into the padding rows change nothing
+    B, Hq, Hkv, S, D = 2, 8, 2, 300, 128
+    say(f"[prefill padded vs dense] B={B} S={S}")
+    q, k, v = (t.to(DEV) for t in
+               inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 8))
+    full = torch.full((B,), S, dtype=torch.int32, device=DEV)
+    o1, l1 = attn.attn_prefill_padded(q, k, v, full)
+    o2, l2 = attn.attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    lens = torch.tensor([77, 300], dtype=torch.int32, device=DEV)
+    o3, l3 = attn.attn_prefill_padded(q, k, v, lens)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[0, :, 77:] = 1000.0
+    o4, l4 = attn.attn_prefill_padded(q2, k2, v2, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+
+
 # ------------------------------------------------------------------- RoPE
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,D", [(1, 8, 2, 300, 128),
