@@ -220,6 +220,19 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
                                          wp.Hq, wp.Hkv, wp.D, out=ov,
                                          with_lse=False)))
     out["prefill_varlen"]["sequences"] = f"{len(lens)} lengths of the decode workload, sum {N}"
+
+    # padded batch: the same lengths, each sequence stored with Smax rows
+    Smax = int(lens.max())
+    B = len(lens)
+    qp = torch.randn(B, wp.Hq, Smax, wp.D, generator=g).to(torch.bfloat16).to(dev)
+    kp2 = torch.randn(B, wp.Hkv, Smax, wp.D, generator=g).to(torch.bfloat16).to(dev)
+    vp2 = torch.randn(B, wp.Hkv, Smax, wp.D, generator=g).to(torch.bfloat16).to(dev)
+    slp = torch.from_numpy(sl.astype("int32")).to(dev)
+    op = torch.empty_like(qp)
+    out["prefill_padded"] = tf(vflops, timed(
+        lambda: attn.attn_prefill_padded(qp, kp2, vp2, slp, out=op,
+                                         with_lse=False)))
+    out["prefill_padded"]["sequences"] = f"the same {B} lengths, padded to {Smax} rows"
     return out
 
 
