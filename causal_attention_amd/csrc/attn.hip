@@ -3,6 +3,8 @@
 #include "attn.h"
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -19,17 +21,18 @@ using attn::kPrefillThreads;
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Orders prefill blocks and sizes the decode split.
 int device_cu_count() {
-  static int cached[64] = {0};
+  // per-device cache; concurrent callers may both query, and store the same
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
                               dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 bool aligned(const void* p, uintptr_t a) {
