@@ -117,6 +117,70 @@ def test_c5_long_context_sampled_rows():
         assert omax[0, h] <= vmax[0, h // G] * (1 + 2 ** -8)
 
 
+def _randn_bf16(shape, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV, dtype=torch.bfloat16)
+
+
+def test_prefill_offsets_beyond_4gb_sampled():
+    """Tensors past 2^31 elements (q, o: 4.4 GB): the last (batch, head)
+    pairs, whose rows start beyond element 2^31, are checked row by row
+    against the oracle; every row is finite."""
+    B, Hq, Hkv, S, D = 64, 32, 8, 8320, 128
+    say(f"[prefill > 4 GB] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    q = _randn_bf16((B, Hq, S, D), 31)
+    k = _randn_bf16((B, Hkv, S, D), 32)
+    v = _randn_bf16((B, Hkv, S, D), 33)
+    assert q.numel() > 2 ** 31
+    o, lse = attn.attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
+    rows = np.array([0, 1, 4095, 4096, S - 2, S - 1])
+    scale = 1 / math.sqrt(D)
+    for b, h in ((B - 1, Hq - 1), (B - 1, 0), (B // 2, Hq // 2)):
+        g = h // (Hq // Hkv)
+        qs = np64(q[b:b + 1, h:h + 1, rows])
+        ro, rl = oracle.prefill_rows(
+            np64(q[b:b + 1, h:h + 1]), np64(k[b:b + 1, g:g + 1]),
+            np64(v[b:b + 1, g:g + 1]), scale, True, rows[None])
+        eo = np.abs(np64(o[b:b + 1, h:h + 1, rows]) - ro).max()
+        el = np.abs(lse[b:b + 1, h:h + 1, rows].cpu().numpy() - rl).max()
+        say(f"   (b={b}, h={h}) rows {rows.tolist()}: max|dO|={eo:.3e} "
+            f"max|dLSE|={el:.3e}")
+        assert qs.shape[2] == len(rows)
+        assert eo <= o_tol("bf16") and el <= LSE_TOL
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_decode_cache_beyond_4gb_sampled():
+    """A packed cache past 2^31 elements per tensor (256 sequences x 8 KV
+    heads x 8256 keys): the last sequences, at the highest offsets, against
+    the oracle."""
+    B, Hq, Hkv, D, L = 256, 32, 8, 128, 8256
+    say(f"[decode > 4 GB] B={B} Hq={Hq} Hkv={Hkv} L={L} D={D}")
+    kc = _randn_bf16((B * Hkv * L * D,), 41)
+    vc = _randn_bf16((B * Hkv * L * D,), 42)
+    assert kc.numel() > 2 ** 31
+    q = _randn_bf16((B, Hq, D), 43)
+    sl = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    o, lse = attn.attn_decode(q, kc, vc, sl, Hkv, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    per = Hkv * L * D
+    for b in (B - 1, B - 2, 0):
+        seg = slice(b * per, (b + 1) * per)
+        ro, rl = oracle.decode(np64(q[b:b + 1]), np64(kc[seg]),
+                               np64(vc[seg]), np.array([L]), 1 / math.sqrt(D),
+                               Hkv)
+        eo = np.abs(np64(o[b:b + 1]) - ro).max()
+        el = np.abs(lse[b:b + 1].cpu().numpy() - rl).max()
+        say(f"   sequence {b}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= 2e-2 and el <= LSE_TOL
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- edge shapes, masks
 
 @pytest.mark.parametrize("S", [1, 2, 7, 63, 64, 65, 127, 129, 1000])
