@@ -174,9 +174,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// One direct-to-LDS load (16 bytes per lane, 1 KB per wave instruction at
+// the wave-uniform LDS address l), issued as inline assembly.  The compiler
+// takes a builtin direct load as possibly aliasing every later LDS read and
+// puts s_waitcnt vmcnt(0) before the first transposed V read of the tile,
+// i.e. it would wait for the NEXT tile's loads (a memory round trip when K/V
+// come from HBM) although they fill the other buffer.  The loop waits for
+// its loads itself (wait_vmem before the barrier of each step), and no load
+// is left in flight when the loop ends.
 __device__ __forceinline__ void lds_direct_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(
-      g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(l));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
