@@ -144,8 +144,8 @@ __device__ __forceinline__ void apply_mask_block(f32x16& x, int j0, int hh,
 // ------------------------------------------------- bf16 / fp16 path
 //
 // K and V tiles go global -> LDS with gfx950's direct loads
-// (global_load_lds_dwordx4: no VGPR staging, each wave instruction fills 1 KB
-// of LDS in lane order), double-buffered so that the next tile streams in
+// (buffer_load_dwordx4 ... lds: no VGPR staging, each wave instruction fills
+// 1 KB of LDS in lane order), double-buffered so that the next tile streams in
 // while the current one is multiplied; one barrier per tile.  Rows are
 // stored with their 16-byte chunks XOR-swizzled so the MFMA operand reads
 // hit distinct LDS banks.  V stays row-major in LDS and its transposed MFMA
@@ -174,18 +174,34 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// One direct-to-LDS load (16 bytes per lane, 1 KB per wave instruction at
-// the wave-uniform LDS address l), issued as inline assembly.  The compiler
-// takes a builtin direct load as possibly aliasing every later LDS read and
-// puts s_waitcnt vmcnt(0) before the first transposed V read of the tile,
-// i.e. it would wait for the NEXT tile's loads (a memory round trip when K/V
-// come from HBM) although they fill the other buffer.  The loop waits for
-// its loads itself (wait_vmem before the barrier of each step), and no load
-// is left in flight when the loop ends.
-__device__ __forceinline__ void lds_direct_load16(const void* g, void* l) {
+// gfx9 raw buffer descriptor: 48-bit base, stride 0, no range limit.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base) {
+  const size_t a = reinterpret_cast<size_t>(base);
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               (unsigned)__builtin_amdgcn_readfirstlane(
+                   (int)((a >> 32) & 0xffff)),
+               0xffffffffu, 0x00020000u};
+}
+
+// One direct-to-LDS load, buffer_load_dwordx4 ... lds: lane i's 16 bytes at
+// base + soff + voff go to LDS at l + 16 i (1 KB per wave instruction; l and
+// soff are wave-uniform).  The descriptor and the tile offset sit in SGPRs,
+// so a load costs no 64-bit address arithmetic per lane.  It is issued as
+// inline assembly: the compiler takes a direct load it can see as possibly
+// aliasing every later LDS read and puts s_waitcnt vmcnt(0) before the first
+// transposed V read of the tile, i.e. it would wait for the NEXT tile's loads
+// (a memory round trip when K/V come from HBM) although they fill the other
+// buffer.  The loop waits for its loads itself (wait_vmem before the barrier
+// of each step), and no load is left in flight when the loop ends.
+__device__ __forceinline__ void lds_buffer_load16(const u32x4& rsrc,
+                                                  unsigned voff, unsigned soff,
+                                                  void* l) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(l));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(m) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(m),
+                  "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
@@ -300,16 +316,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     koffb[i] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2;
     voffb[i] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2;
   }
+  const u32x4 krs = buffer_rsrc(Kp), vrs = buffer_rsrc(Vp);
   auto issue_tile = [&](int jt, T* Kd, T* Vd) {
     const int j0 = jt * BN;
-    const char* Kb = reinterpret_cast<const char*>(Kp + (size_t)j0 * D);
-    const char* Vb = reinterpret_cast<const char*>(Vp + (size_t)j0 * D);
+    const unsigned soff = (unsigned)j0 * D * 2;   // tile offset in bytes
     if (j0 + BN <= S) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const int r0 = (w * IPW + i) * RPI;
-        lds_direct_load16(Kb + koffb[i], Kd + r0 * D);
-        lds_direct_load16(Vb + voffb[i], Vd + r0 * D);
+        lds_buffer_load16(krs, koffb[i], soff, Kd + r0 * D);
+        lds_buffer_load16(vrs, voffb[i], soff, Vd + r0 * D);
       }
     } else {
 #pragma unroll
@@ -317,8 +333,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
         const int r0 = (w * IPW + i) * RPI;
         const int row = r0 + lane / CPR;
         const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
-        lds_direct_load16(Kb + koffb[i] + back, Kd + r0 * D);
-        lds_direct_load16(Vb + voffb[i] + back, Vd + r0 * D);
+        lds_buffer_load16(krs, koffb[i] + back, soff, Kd + r0 * D);
+        lds_buffer_load16(vrs, voffb[i] + back, soff, Vd + r0 * D);
       }
     }
   };
