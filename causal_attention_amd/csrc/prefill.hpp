@@ -193,6 +193,33 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base) {
 // (a memory round trip when K/V come from HBM) although they fill the other
 // buffer.  The loop waits for its loads itself (wait_vmem before the barrier
 // of each step), and no load is left in flight when the loop ends.
+// A wave's IPW loads of one tile, into consecutive 1 KB LDS blocks from l,
+// with M0 set once: load i carries the immediate offset i*1024, which the
+// hardware adds to both the LDS and the memory address, so voff[i] holds
+// lane offset of load i minus i*1024 (never negative: the wave's rows of
+// load i start i KB into the tile).
+template <int IPW>
+__device__ __forceinline__ void lds_buffer_load16_run(const u32x4& rsrc,
+                                                      const unsigned (&voff)[IPW],
+                                                      unsigned soff, void* l) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(l));
+  const unsigned so = __builtin_amdgcn_readfirstlane(soff);
+  static_assert(IPW == 2 || IPW == 4, "loads per wave");
+  if constexpr (IPW == 4)
+    asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %5, %6 offen lds\n\t"
+                 "buffer_load_dwordx4 %1, %5, %6 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, %6 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, %6 offen offset:3072 lds"
+                 :: "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                    "s"(m), "s"(rsrc), "s"(so) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %3, %4 offen lds\n\t"
+                 "buffer_load_dwordx4 %1, %3, %4 offen offset:1024 lds"
+                 :: "v"(voff[0]), "v"(voff[1]),
+                    "s"(m), "s"(rsrc), "s"(so) : "memory", "m0");
+}
 __device__ __forceinline__ void lds_buffer_load16(const u32x4& rsrc,
                                                   unsigned voff, unsigned soff,
                                                   void* l) {
@@ -309,24 +336,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   // Issue the direct loads of key tile jt into (Kd, Vd).  Rows past the end
   // of the sequence load row S-1 (their scores are masked to -inf, so their
   // values are multiplied by p = 0).
-  unsigned koffb[IPW], voffb[IPW];
+  unsigned koffb[IPW], voffb[IPW], koffr[IPW], voffr[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (w * IPW + i) * RPI + lane / CPR, pos = lane % CPR;
     koffb[i] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2;
     voffb[i] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2;
+    koffr[i] = koffb[i] - i * 1024;
+    voffr[i] = voffb[i] - i * 1024;
   }
   const u32x4 krs = buffer_rsrc(Kp), vrs = buffer_rsrc(Vp);
   auto issue_tile = [&](int jt, T* Kd, T* Vd) {
     const int j0 = jt * BN;
     const unsigned soff = (unsigned)j0 * D * 2;   // tile offset in bytes
     if (j0 + BN <= S) {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int r0 = (w * IPW + i) * RPI;
-        lds_buffer_load16(krs, koffb[i], soff, Kd + r0 * D);
-        lds_buffer_load16(vrs, voffb[i], soff, Vd + r0 * D);
-      }
+      static_assert(RPI * D * 2 == 1024, "1 KB per load");
+      lds_buffer_load16_run<IPW>(krs, koffr, soff, Kd + w * IPW * RPI * D);
+      lds_buffer_load16_run<IPW>(vrs, voffr, soff, Vd + w * IPW * RPI * D);
     } else {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
