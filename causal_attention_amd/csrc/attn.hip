@@ -40,6 +40,9 @@ bool aligned(const void* p, uintptr_t a) {
 }
 
 // Common shape checks of both prefill entry points.
+// Largest S * D of one head's rows (2^30 elements: 2 GB of 16-bit data).
+constexpr long long kMaxHeadElems = 1LL << 30;
+
 int check_prefill(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, int B, int Hq, int Hkv, int S, int D,
                   float scale, bool* empty) {
@@ -51,6 +54,9 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o,
   // Grid size: one workgroup per (batch, query head, 128-row tile).
   const long long tiles = ((long long)S + kPrefillBM - 1) / kPrefillBM;
   if ((long long)B * Hq * tiles > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  // The K and V rows of one (batch, KV head) are addressed with 32-bit byte
+  // offsets from their first row.
+  if ((long long)S * D > kMaxHeadElems) return ATTN_ERR_SHAPE;
   if (B == 0 || S == 0) {
     *empty = true;
     return ATTN_OK;

@@ -66,8 +66,10 @@ typedef enum {
  *          setting; the fused Triton kernel of the attention-fusion page,
  *          section 3.2, applies it to qk before the softmax).
  *   causal: nonzero for the causal mask j <= i, zero for no mask.
- * Any S >= 0 is accepted (tail tiles are masked, as section 6.1 of the
- * attention-fusion page requires).  D must be 64 or 128.
+ * Any S >= 0 with S * D <= 2^30 is accepted (tail tiles are masked, as
+ * section 6.1 of the attention-fusion page requires); the rows of one head
+ * are addressed with 32-bit byte offsets, so a larger S is ATTN_ERR_SHAPE.
+ * D must be 64 or 128.
  */
 int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  float* lse, int B, int Hq, int Hkv, int S, int D,

@@ -71,6 +71,9 @@ def test_prefill_argument_errors(fn):
     assert prefill(fn, scale=-0.125) == -9
     # grid too large for one launch
     assert prefill(fn, B=65536, Hq=1024, Hkv=1, S=1 << 20) == -2
+    # one head's rows past 32-bit byte offsets (S * D > 2^30)
+    assert prefill(fn, B=1, Hq=1, Hkv=1, S=(1 << 23) + 1, D=128) == -2
+    assert prefill(fn, B=1, Hq=1, Hkv=1, S=(1 << 24) + 1, D=64) == -2
 
 
 @pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f16",
