@@ -74,6 +74,8 @@ def test_prefill_argument_errors(fn):
     # one head's rows past 32-bit byte offsets (S * D > 2^30)
     assert prefill(fn, B=1, Hq=1, Hkv=1, S=(1 << 23) + 1, D=128) == -2
     assert prefill(fn, B=1, Hq=1, Hkv=1, S=(1 << 24) + 1, D=64) == -2
+    # exactly at the limit the shape is accepted (and the NULL q is reported)
+    assert prefill(fn, B=1, Hq=1, Hkv=1, S=1 << 23, D=128, q=None) == -1
 
 
 @pytest.mark.parametrize("fn", ["attn_prefill", "attn_prefill_f16",
