@@ -124,7 +124,19 @@ def cpu_baseline(wp, wd):
     t0 = time.perf_counter()
     oracle.decode(q, kc, vc, sl, wd.scale, wd.Hkv)
     td = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = sorted({f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+                   for i in info if i.get("user_api") == "blas"})
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": pflops / tp / 1e12,
         "unit": "TFLOP/s",
@@ -134,6 +146,8 @@ def cpu_baseline(wp, wd):
                    "numpy fp64"),
         "decode_GBps": decode_bytes(sl, wd.Hq, wd.Hkv, wd.D) / td / 1e9,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model,
+        "blas": ", ".join(blas) or "unknown",
     }
 
 
