@@ -1,22 +1,25 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
-One step = one causal GQA prefill (batch 4, 8 query heads over 2 KV heads,
-head_dim 128, seq 2048, bf16) followed by one split-K decode (batch 32, same
-heads, per-sequence cache length uniform in [256, 4096] from seed 0, bf16),
-each through the C ABI on torch's current stream.  Inputs are seeded
-synthetic tensors resident in HBM before timing; several input copies are
-rotated so consecutive steps do not find their inputs in the 256 MB
-last-level cache.
+One step = one causal GQA prefill at long context (batch 1, 8 query heads
+over 2 KV heads, head_dim 128, seq 32768, bf16) followed by one split-K
+decode (batch 32, same heads, per-sequence cache length uniform in
+[256, 4096] from seed 0, bf16), each through the C ABI on torch's current
+stream.  Inputs are seeded synthetic tensors resident in HBM before timing;
+enough input copies are rotated that no launch finds its inputs in the
+256 MB last-level cache.
 
-Prints ONE JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
-(4*D per visible query/key pair, causal pairs only) over the prefill kernel's
-average duration measured with HIP events; the decode's KV-cache GB/s
-(K and V bytes read once per KV head, plus q and o) is in ``decode``.  Both
-carry a ``roofline`` object against MI355X's published peaks (2.5 PFLOP/s
-dense bf16 MFMA, 8 TB/s HBM3E).  ``cpu_baseline`` times the fp64 CPU oracle
-on the host on a bounded sample of the same workload.  With ``--extras`` the
-line also carries ``extras``: the widened paths (fp16 storage, RoPE, ragged
-batch) timed on the same shapes.
+Prints ONE JSON line.  ``value`` is the prefill's algorithmic TFLOP/s (4*D
+per visible query/key pair, causal pairs only) over the prefill kernel's
+mean duration measured with HIP events around each launch; the decode's
+KV-cache GB/s (K and V bytes read once per KV head, plus q and o) is in
+``decode``.  Both carry a ``roofline`` object against MI355X's published
+peaks (2.5 PFLOP/s dense bf16 MFMA, 8 TB/s HBM3E) with the mean, median
+and minimum launch time.  ``side_configs`` times the other prefill workloads
+(batch 4 at seq 2048 by default) the same way, each against its own dtype's
+peak.  ``cpu_baseline`` times the fp64 CPU oracle on the host on a bounded
+sample of the same workload.  With ``--extras`` the line also carries
+``extras``: the widened paths (fp16 storage, RoPE, ragged batch) timed on
+the shapes of the batch-4 prefill and the decode.
 """
 
 import argparse
@@ -31,7 +34,30 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+LLC_BYTES = 256 * 2 ** 20       # MI355X last-level (Infinity) cache
+
+
+def peak_tflops(dtype):
+    return PEAK_FP32_MATRIX_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+
+
+def copies_for(nbytes, at_least=2, at_most=64):
+    """Input copies to rotate so that a copy is reused only after more than
+    the last-level cache's worth of other inputs has been read."""
+    return int(min(at_most, max(at_least, -(-int(1.2 * LLC_BYTES) // max(
+        1, nbytes)) + 1)))
+
+
+def launch_stats(ms):
+    """mean / median / min of per-launch times (ms) in microseconds."""
+    xs = sorted(ms)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"mean_us": round(1e3 * sum(xs) / n, 3),
+            "median_us": round(1e3 * med, 3),
+            "min_us": round(1e3 * xs[0], 3), "launches": n}
 
 
 def prefill_flops(B, Hq, S, D, causal=True):
@@ -40,6 +66,7 @@ def prefill_flops(B, Hq, S, D, causal=True):
 
 
 def prefill_bytes(B, Hq, Hkv, S, D, elt=2):
+    """Q, K, V read once, O and the fp32 LSE written once."""
     return (B * Hq * S * D * 2 + B * Hkv * S * D * 2) * elt + B * Hq * S * 4
 
 
@@ -77,6 +104,15 @@ def measured_traffic():
     if kv.get("kernel_sources_sha256") != kernel_source_hash():
         return {}
     return kv
+
+
+def traffic_for(tr, key, workload):
+    """Bytes per launch recorded for ``key`` if they were taken on
+    ``workload``, else None."""
+    if tr.get(key + "_workload") != workload or key + "_hbm_bytes_per_launch" \
+            not in tr:
+        return None
+    return int(tr[key + "_hbm_bytes_per_launch"])
 
 
 def copy_calibration(mbytes, reps=5):
@@ -250,15 +286,73 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
     return out
 
 
+
+
+def time_prefill(attn, inputs, torch, dev, w, steps, warmup):
+    """Event-timed launches of one prefill workload through prepared C-ABI
+    calls, rotating input copies; returns (stats, copies)."""
+    q, k, v = inputs.prefill_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype,
+                                    w.sigma, w.seed)
+    elt = 4 if w.dtype == "f32" else 2
+    R = copies_for(prefill_bytes(w.B, w.Hq, w.Hkv, w.S, w.D, elt))
+    ins = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(R)]
+    outs = [torch.empty_like(ins[0][0]) for _ in range(R)]
+    lses = [torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+            for _ in range(R)]
+    calls = [attn.prepare_prefill(*ins[r], outs[r], lses[r], causal=w.causal,
+                                  scale=w.scale) for r in range(R)]
+    for i in range(warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        calls[i % R]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return launch_stats([e[0].elapsed_time(e[1]) for e in ev]), R
+
+
+def prefill_record(w, st, R, traffic=None):
+    """The roofline object of one prefill workload from its launch stats."""
+    elt = 4 if w.dtype == "f32" else 2
+    flops = prefill_flops(w.B, w.Hq, w.S, w.D, w.causal)
+    peak = peak_tflops(w.dtype)
+    tf = flops / (st["mean_us"] * 1e-6) / 1e12
+    return {
+        "bound": "mfma",
+        "kernel": "attn_prefill_f32_kernel" if w.dtype == "f32"
+                  else "attn_prefill_kernel",
+        "achieved": round(tf, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(tf / peak, 4),
+        "traffic": traffic,
+        "traffic_unit": "HBM bytes per launch",
+        "algorithmic_bytes": prefill_bytes(w.B, w.Hq, w.Hkv, w.S, w.D, elt),
+        "flops_per_launch": flops,
+        **st,
+        "median_TFLOPs": round(flops / (st["median_us"] * 1e-6) / 1e12, 3),
+        "best_TFLOPs": round(flops / (st["min_us"] * 1e-6) / 1e12, 3),
+        "input_copies_rotated": R,
+        "shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                  "dtype": w.dtype, "causal": w.causal, "sigma": w.sigma,
+                  "seed": w.seed},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rotate", type=int, default=4,
-                    help="input copies cycled through (defeats the LLC)")
-    ap.add_argument("--prefill", default="c3_gqa_b4_s2048")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill", default="c5_gqa_s32768",
+                    help="prefill workload of the step (value / roofline)")
     ap.add_argument("--decode", default="c4_decode_b32")
+    ap.add_argument("--side", default="c3_gqa_b4_s2048",
+                    help="comma-separated prefill workloads timed after the "
+                    "step, reported under side_configs ('' for none)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -268,7 +362,7 @@ def main():
                     help="also time the fp16 / RoPE / ragged-batch paths "
                     "(reported under \"extras\"; off by default so the "
                     "kernel statistics of the default run hold only the "
-                    "main step's launches)")
+                    "step's and side configs' launches)")
     args = ap.parse_args()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
@@ -287,18 +381,22 @@ def main():
     torch.cuda.set_device(dev)
     wp = inputs.WORKLOADS[args.prefill]
     wd = inputs.WORKLOADS[args.decode]
+    side = [inputs.WORKLOADS[n] for n in args.side.split(",") if n]
 
+    # ---- the step: prefill + decode, copies rotated separately
     q, k, v = inputs.prefill_inputs(wp.B, wp.Hq, wp.Hkv, wp.S, wp.D,
                                     wp.dtype, wp.sigma, wp.seed)
     sl, dq, kc, vc = inputs.workload_inputs(wd)
-    R = max(1, args.rotate)
-    P = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(R)]
-    Dd = [tuple(t.to(dev) for t in (dq, kc, vc)) for _ in range(R)]
+    Rp = copies_for(prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.S, wp.D))
+    dbytes = decode_bytes(sl, wd.Hq, wd.Hkv, wd.D)
+    Rd = copies_for(dbytes, at_least=5)
+    P = [tuple(t.to(dev) for t in (q, k, v)) for _ in range(Rp)]
+    Dd = [tuple(t.to(dev) for t in (dq, kc, vc)) for _ in range(Rd)]
     sl_d = torch.from_numpy(sl).to(dev)
-    po = [torch.empty_like(P[0][0]) for _ in range(R)]
+    po = [torch.empty_like(P[0][0]) for _ in range(Rp)]
     plse = [torch.empty((wp.B, wp.Hq, wp.S), dtype=torch.float32, device=dev)
-            for _ in range(R)]
-    do = [torch.empty_like(Dd[0][0]) for _ in range(R)]
+            for _ in range(Rp)]
+    do = [torch.empty_like(Dd[0][0]) for _ in range(Rd)]
     ws = attn.new_decode_workspace(wd.B, wd.Hq, wd.Hkv, wd.D,
                                    args.num_splits, dev)
     ns = args.num_splits or attn.attn_decode_auto_splits(wd.B, wd.Hkv)
@@ -306,19 +404,18 @@ def main():
     # Arguments are converted once; each launch is then a single C call, so
     # the host stays ahead of the GPU and the events time the kernels.
     pre = [attn.prepare_prefill(*P[r], po[r], plse[r], causal=True,
-                                scale=wp.scale) for r in range(R)]
+                                scale=wp.scale) for r in range(Rp)]
     dec = [attn.prepare_decode(*Dd[r], sl_d, do[r], wd.Hkv, ws,
                                num_splits=ns, scale=wd.scale)
-           for r in range(R)]
+           for r in range(Rd)]
 
     def step(i, ev=None):
-        r = i % R
         if ev is not None:
             ev[0].record()
-        pre[r]()
+        pre[i % Rp]()
         if ev is not None:
             ev[1].record()
-        dec[r]()
+        dec[i % Rd]()
         if ev is not None:
             ev[2].record()
 
@@ -335,28 +432,37 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    pst = launch_stats([e[0].elapsed_time(e[1]) for e in evs])
+    dst = launch_stats([e[1].elapsed_time(e[2]) for e in evs])
 
-    # The decode as a serving loop runs it: the steps of the R input copies
-    # (standing in for R layers of one token) captured once in a hipGraph
-    # and replayed; reported per decode step.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for r in range(R):
+    # ---- side configs (other prefill workloads), timed the same way
+    side_rec = {}
+    for w in side:
+        st, R = time_prefill(attn, inputs, torch, dev, w, K, args.warmup)
+        rec = prefill_record(w, st, R)
+        rec["workgroups"] = attn.prefill_workgroups(w.B, w.Hq, w.S, w.D)
+        side_rec[w.name] = rec
+
+    # ---- the decode as a serving loop runs it: the Rd rotated decode
+    # calls (standing in for Rd layers of one token) captured once in a
+    # hipGraph and replayed; reported per decode
+    sstream = torch.cuda.Stream()
+    sstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(sstream):
+        for r in range(Rd):
             attn.prepare_decode(*Dd[r], sl_d, do[r], wd.Hkv, ws,
                                 num_splits=ns, scale=wd.scale)()
-    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.current_stream().wait_stream(sstream)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for r in range(R):
+        for r in range(Rd):
             attn.prepare_decode(*Dd[r], sl_d, do[r], wd.Hkv, ws,
                                 num_splits=ns, scale=wd.scale)()
     torch.cuda.synchronize()
-    for i in range(max(1, args.warmup // R)):
-        graph.replay()
+    graph.replay()
     torch.cuda.synchronize()
-    KG = max(1, K // R)
+    KG = max(2, K // Rd)
     gevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
             for _ in range(KG)]
     for i in range(KG):
@@ -364,25 +470,18 @@ def main():
         graph.replay()
         gevs[i][1].record()
     torch.cuda.synchronize()
-    dg_avg = sum(e[0].elapsed_time(e[1]) for e in gevs) / (KG * R)
+    gst = launch_stats([e[0].elapsed_time(e[1]) / Rd for e in gevs])
 
-    pf_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dc_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    pf_avg = sum(pf_ms) / K
-    dc_avg = sum(dc_ms) / K
-    flops = prefill_flops(wp.B, wp.Hq, wp.S, wp.D)
-    dbytes = decode_bytes(sl, wd.Hq, wd.Hkv, wd.D)
-    p_tflops = flops / (pf_avg * 1e-3) / 1e12
-    d_gbs = dbytes / (dc_avg * 1e-3) / 1e9
-
-    tr = measured_traffic() if (wp.name, wd.name) == (
-        "c3_gqa_b4_s2048", "c4_decode_b32") else {}
-    p_traffic = int(tr["prefill_hbm_bytes_per_launch"]) if tr else None
-    d_traffic = int(tr["decode_hbm_bytes_per_launch"]) if tr else None
+    tr = measured_traffic()
+    prec = prefill_record(wp, pst, Rp, traffic_for(tr, "prefill", wp.name))
+    prec.pop("shape")
+    prec["workgroups"] = attn.prefill_workgroups(wp.B, wp.Hq, wp.S, wp.D)
+    d_gbs = dbytes / (dst["mean_us"] * 1e-6) / 1e9
+    g_gbs = dbytes / (gst["mean_us"] * 1e-6) / 1e9
     out = {
         "metric": "prefill attention TFLOP/s + decode KV-cache GB/s, "
                   "% of MI355X roofline",
-        "value": round(p_tflops, 3),
+        "value": prec["achieved"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
@@ -401,26 +500,15 @@ def main():
             "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D,
                        "seqlens": "U[256,4096] seed 0",
                        "sum_seqlens": int(sl.sum()), "num_splits": ns},
-            "input_copies_rotated": R,
+            "input_copies_rotated": {"prefill": Rp, "decode": Rd},
+            "timing": "HIP events around each launch on the launching "
+                      "stream; value and roofline use the mean launch time, "
+                      "median and min beside it",
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_prefill_kernel",
-            "achieved": round(p_tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": p_traffic,
-            "traffic_unit": "HBM bytes per launch",
-            "algorithmic_bytes": prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.S,
-                                               wp.D),
-            "flops_per_launch": flops,
-            "avg_launch_us": round(pf_avg * 1e3, 3),
-        },
+        "roofline": prec,
         "decode": {
             "value": round(d_gbs, 2),
             "unit": "GB/s",
-            "avg_us": round(dc_avg * 1e3, 3),
             "roofline": {
                 "bound": "hbm",
                 "kernel": "attn_decode_split_kernel + "
@@ -429,20 +517,28 @@ def main():
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": round(d_gbs / PEAK_HBM_GBS, 4),
-                "traffic": d_traffic,
+                "traffic": traffic_for(tr, "decode", wd.name),
                 "traffic_unit": "HBM bytes per launch (split + combine)",
                 "bytes_per_launch": dbytes,
+                **dst,
+                "median_GBps": round(
+                    dbytes / (dst["median_us"] * 1e-6) / 1e9, 2),
+                "best_GBps": round(dbytes / (dst["min_us"] * 1e-6) / 1e9, 2),
             },
             "graph": {
-                "what": f"{R} decode steps (one per input copy) captured "
-                        "in one hipGraph and replayed; time per step",
-                "avg_us": round(dg_avg * 1e3, 3),
-                "GBps": round(dbytes / (dg_avg * 1e-3) / 1e9, 2),
+                "what": f"{Rd} decode calls (one per rotated cache copy) "
+                        "captured in one hipGraph and replayed; time per "
+                        "decode",
+                **gst,
+                "GBps": round(g_gbs, 2),
+                "frac": round(g_gbs / PEAK_HBM_GBS, 4),
             },
         },
+        "side_configs": side_rec,
     }
     if args.extras:
-        out["extras"] = extras(attn, inputs, torch, dev, wp, wd)
+        out["extras"] = extras(attn, inputs, torch, dev,
+                               inputs.WORKLOADS["c3_gqa_b4_s2048"], wd)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp, wd)
     print(json.dumps(out), flush=True)

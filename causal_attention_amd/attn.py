@@ -72,6 +72,11 @@ def lib():
         L.attn_prefill_padded.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
                                           i, f, i, vp]
         L.attn_prefill_padded.restype = i
+        for n in ("attn_prefill_rope_f16", "attn_prefill_varlen_f16",
+                  "attn_prefill_padded_f16", "attn_kv_append_f16",
+                  "attn_decode_padded_f16"):
+            fn, base = getattr(L, n), getattr(L, n[:-4])
+            fn.argtypes, fn.restype = base.argtypes, base.restype
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -91,10 +96,10 @@ def _stream():
 
 
 def _check(t, name, dtype, ndim):
+    """Type, dtype, rank and contiguity of one tensor argument (the device
+    is checked by ``_on_gpu`` once every shape has been checked)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
@@ -103,9 +108,52 @@ def _check(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _fn(base, dtype):
+    """The C entry point for a 16-bit storage type: ``base`` for bf16,
+    ``base_f16`` for fp16."""
+    if dtype == torch.bfloat16:
+        return base
+    if dtype == torch.float16:
+        return base + "_f16"
+    raise ValueError(f"{base}: tensors must be bfloat16 or float16, "
+                     f"got {dtype}")
+
+
 _PREFILL_FN = {torch.bfloat16: "attn_prefill", torch.float16: "attn_prefill_f16",
                torch.float32: "attn_prefill_f32"}
 _DECODE_FN = {torch.bfloat16: "attn_decode", torch.float16: "attn_decode_f16"}
+
+
+def _prefill_shapes(q, k, v, dtype):
+    _check(q, "q", dtype, 4)
+    _check(k, "k", dtype, 4)
+    _check(v, "v", dtype, 4)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    return B, Hq, Hkv, S, D
+
+
+def _lse_arg(lse, with_lse, shape, like):
+    if with_lse and lse is None:
+        lse = torch.empty(shape, dtype=torch.float32, device=like.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, len(shape))
+        _shape(lse, "lse", shape)
+    return lse
 
 
 def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
@@ -120,31 +168,20 @@ def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
     dtype = q.dtype
     if dtype not in _PREFILL_FN:
         raise ValueError("q must be bfloat16, float16 or float32")
-    _check(q, "q", dtype, 4)
-    _check(k, "k", dtype, 4)
-    _check(v, "v", dtype, 4)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    B, Hq, Hkv, S, D = _prefill_shapes(q, k, v, dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", dtype, 4)
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
-    if with_lse and lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 3)
-        if lse.shape != (B, Hq, S):
-            raise ValueError("lse must be [B,Hq,S]")
+    _shape(out, "out", q.shape)
+    lse = _lse_arg(lse, with_lse, (B, Hq, S), q)
+    _on_gpu(q=q, k=k, v=v, out=out, lse=lse)
     fn = getattr(lib(), _PREFILL_FN[dtype])
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
             D, float(scale), int(bool(causal)), _stream())
     if st != 0:
-        raise AttnError(st, fn.__name__)
+        raise AttnError(st, _PREFILL_FN[dtype])
     return out, lse
 
 
@@ -165,6 +202,19 @@ def new_decode_workspace(B, Hq, Hkv, D, num_splits=0, device="cuda"):
     return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
 
 
+def _decode_outputs(q, out, lse, with_lse, workspace, Hkv, num_splits):
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.dtype, 3)
+    _shape(out, "out", q.shape)
+    lse = _lse_arg(lse, with_lse, (B, Hq), q)
+    if workspace is None:
+        workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
+    _check(workspace, "workspace", torch.uint8, 1)
+    return out, lse, workspace
+
+
 def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
                 out=None, with_lse=False, lse=None, workspace=None):
     """Split-K decode attention over a packed per-sequence KV cache.
@@ -183,23 +233,15 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
     _check(vcache, "vcache", dtype, None)
     _check(seqlens, "seqlens", torch.int32, 1)
     B, Hq, D = q.shape
-    if seqlens.shape[0] != B:
-        raise ValueError("seqlens must have B entries")
+    _shape(seqlens, "seqlens", (B,))
     if kcache.numel() != vcache.numel():
         raise ValueError("kcache and vcache must have the same size")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    _check(out, "out", dtype, 3)
-    if with_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 2)
-    need = attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) if B else 0
-    if workspace is None:
-        workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
-    _check(workspace, "workspace", torch.uint8, 1)
+    out, lse, workspace = _decode_outputs(q, out, lse, with_lse, workspace,
+                                          Hkv, num_splits)
+    _on_gpu(q=q, kcache=kcache, vcache=vcache, seqlens=seqlens, out=out,
+            lse=lse, workspace=workspace)
     fn = getattr(lib(), _DECODE_FN[dtype])
     st = fn(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B,
             Hq, Hkv, D, float(scale), int(num_splits), _ptr(lse),
@@ -211,42 +253,40 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
 
 def attn_prefill_rope(q, k, v, rope_base, causal=True, scale=None, out=None,
                       lse=None, with_lse=True, k_rot=None):
-    """Prefill attention of RoPE(q), RoPE(k), v at positions 0..S-1 (bf16).
+    """Prefill attention of RoPE(q), RoPE(k), v at positions 0..S-1, bf16
+    (``attn_prefill_rope``) or fp16 (``attn_prefill_rope_f16``).
 
     Returns (o, lse, k_rot) where k_rot [B,Hkv,S,D] holds the rotated keys
     (allocated when not given).  See ``attn_prefill_rope`` in attn.h.
     """
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, 4)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    name = _fn("attn_prefill_rope", q.dtype)
+    B, Hq, Hkv, S, D = _prefill_shapes(q, k, v, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", torch.bfloat16, 4)
+    _check(out, "out", q.dtype, 4)
+    _shape(out, "out", q.shape)
     if k_rot is None:
         k_rot = torch.empty_like(k)
-    _check(k_rot, "k_rot", torch.bfloat16, 4)
-    if with_lse and lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 3)
-    st = lib().attn_prefill_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                 _ptr(lse), _ptr(k_rot), B, Hq, Hkv, S, D,
-                                 float(scale), int(bool(causal)),
-                                 float(rope_base), _stream())
+    _check(k_rot, "k_rot", q.dtype, 4)
+    _shape(k_rot, "k_rot", k.shape)
+    lse = _lse_arg(lse, with_lse, (B, Hq, S), q)
+    _on_gpu(q=q, k=k, v=v, out=out, k_rot=k_rot, lse=lse)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                              _ptr(lse), _ptr(k_rot), B, Hq, Hkv, S, D,
+                              float(scale), int(bool(causal)),
+                              float(rope_base), _stream())
     if st != 0:
-        raise AttnError(st, "attn_prefill_rope")
+        raise AttnError(st, name)
     return out, lse, k_rot
 
 
 def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
                         causal=True, scale=None, out=None, lse=None,
                         with_lse=True):
-    """Prefill of a ragged batch (bf16), each sequence attended on its own.
+    """Prefill of a ragged batch (bf16 or fp16), each sequence attended on
+    its own.
 
     cu_seqlens int32 [B+1] on the GPU (cu[0] = 0, S_b = cu[b+1] - cu[b]);
     q (and o) hold [Hq, S_b, D] blocks at element offset Hq*D*cu[b], k and v
@@ -254,8 +294,9 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
     elements); lse [Hq*cu[B]] holds [Hq, S_b] blocks at offset Hq*cu[b].
     ``max_seqlen`` bounds every S_b.  Returns (o, lse).
     """
+    name = _fn("attn_prefill_varlen", q.dtype)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, None)
+        _check(t, n, q.dtype, None)
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
     B = cu_seqlens.shape[0] - 1
     if B < 0:
@@ -269,7 +310,7 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", torch.bfloat16, None)
+    _check(out, "out", q.dtype, None)
     if out.numel() != q.numel():
         raise ValueError("out must have q's size")
     if with_lse and lse is None:
@@ -278,111 +319,103 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, Hq, Hkv, D,
         _check(lse, "lse", torch.float32, None)
         if lse.numel() != Hq * N:
             raise ValueError("lse must have Hq * cu[B] entries")
-    st = lib().attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                   _ptr(lse), _ptr(cu_seqlens), B,
-                                   int(max_seqlen), Hq, Hkv, D, float(scale),
-                                   int(bool(causal)), _stream())
+    _on_gpu(q=q, k=k, v=v, cu_seqlens=cu_seqlens, out=out, lse=lse)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                              _ptr(lse), _ptr(cu_seqlens), B,
+                              int(max_seqlen), Hq, Hkv, D, float(scale),
+                              int(bool(causal)), _stream())
     if st != 0:
-        raise AttnError(st, "attn_prefill_varlen")
+        raise AttnError(st, name)
     return out, lse
 
 
 def attn_prefill_padded(q, k, v, seqlens, causal=True, scale=None, out=None,
                         lse=None, with_lse=True):
-    """Prefill of a padded batch (bf16): q [B,Hq,S,D], k, v [B,Hkv,S,D] as
-    for ``attn_prefill``, with seqlens int32 [B] on the GPU giving the valid
-    rows L_b of each sequence (clamped to [0, S]).  Rows i < L_b attend keys
-    j < L_b only; padding rows get o = 0 and lse = -inf.  Returns (o, lse).
+    """Prefill of a padded batch (bf16 or fp16): q [B,Hq,S,D], k, v
+    [B,Hkv,S,D] as for ``attn_prefill``, with seqlens int32 [B] on the GPU
+    giving the valid rows L_b of each sequence (clamped to [0, S]).  Rows
+    i < L_b attend keys j < L_b only; padding rows get o = 0 and
+    lse = -inf.  Returns (o, lse).
     """
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, 4)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError(f"k, v must be [B,Hkv,S,D] = [{B},{Hkv},{S},{D}]")
+    name = _fn("attn_prefill_padded", q.dtype)
+    B, Hq, Hkv, S, D = _prefill_shapes(q, k, v, q.dtype)
     _check(seqlens, "seqlens", torch.int32, 1)
-    if seqlens.shape[0] != B:
-        raise ValueError("seqlens must have B entries")
+    _shape(seqlens, "seqlens", (B,))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", torch.bfloat16, 4)
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
-    if with_lse and lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 3)
-        if lse.shape != (B, Hq, S):
-            raise ValueError("lse must be [B,Hq,S]")
-    st = lib().attn_prefill_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                   _ptr(lse), _ptr(seqlens), B, Hq, Hkv, S, D,
-                                   float(scale), int(bool(causal)), _stream())
+    _check(out, "out", q.dtype, 4)
+    _shape(out, "out", q.shape)
+    lse = _lse_arg(lse, with_lse, (B, Hq, S), q)
+    _on_gpu(q=q, k=k, v=v, seqlens=seqlens, out=out, lse=lse)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                              _ptr(lse), _ptr(seqlens), B, Hq, Hkv, S, D,
+                              float(scale), int(bool(causal)), _stream())
     if st != 0:
-        raise AttnError(st, "attn_prefill_padded")
+        raise AttnError(st, name)
     return out, lse
 
 
 def attn_kv_append(k_new, v_new, kcache, vcache, seqlens, rope_base=0.0):
     """Append one token per sequence to a padded KV cache (in place).
 
-    k_new, v_new [B,Hkv,D]; kcache, vcache [B,Hkv,cap,D] of the same 16-bit
-    dtype; seqlens int32 [B] on the GPU, advanced by one for every sequence
-    that is not full.  ``rope_base`` > 0 stores k rotated to its position.
-    Launches on the current stream (graph-capturable).
+    k_new, v_new [B,Hkv,D]; kcache, vcache [B,Hkv,cap,D], all bf16 (calls
+    ``attn_kv_append``) or all fp16 (``attn_kv_append_f16``); seqlens int32
+    [B] on the GPU, advanced by one for every sequence that is not full.
+    ``rope_base`` > 0 stores k rotated to its position.  Launches on the
+    current stream (graph-capturable).
     """
     dtype = k_new.dtype
-    if dtype not in (torch.bfloat16, torch.float16):
-        raise ValueError("k_new must be bfloat16 or float16")
+    name = _fn("attn_kv_append", dtype)
     _check(k_new, "k_new", dtype, 3)
     _check(v_new, "v_new", dtype, 3)
     _check(kcache, "kcache", dtype, 4)
     _check(vcache, "vcache", dtype, 4)
     _check(seqlens, "seqlens", torch.int32, 1)
     B, Hkv, cap, D = kcache.shape
-    if (k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or
-            vcache.shape != kcache.shape or seqlens.shape[0] != B):
-        raise ValueError("inconsistent kv append shapes")
-    st = lib().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(kcache),
+    _shape(k_new, "k_new", (B, Hkv, D))
+    _shape(v_new, "v_new", (B, Hkv, D))
+    _shape(vcache, "vcache", kcache.shape)
+    _shape(seqlens, "seqlens", (B,))
+    _on_gpu(k_new=k_new, v_new=v_new, kcache=kcache, vcache=vcache,
+            seqlens=seqlens)
+    st = getattr(lib(), name)(_ptr(k_new), _ptr(v_new), _ptr(kcache),
                               _ptr(vcache), _ptr(seqlens), B, Hkv, D, cap,
                               float(rope_base), _stream())
     if st != 0:
-        raise AttnError(st, "attn_kv_append")
+        raise AttnError(st, name)
 
 
 def attn_decode_padded(q, kcache, vcache, seqlens, num_splits=0, scale=None,
                        out=None, with_lse=False, lse=None, workspace=None,
                        rope_base=0.0):
-    """Decode attention over a padded cache [B,Hkv,cap,D] (bf16), with
-    L_b = min(seqlens[b], cap); otherwise as ``attn_decode``.  ``rope_base``
-    > 0 rotates each query to its position L_b - 1 in the kernel."""
-    _check(q, "q", torch.bfloat16, 3)
-    _check(kcache, "kcache", torch.bfloat16, 4)
-    _check(vcache, "vcache", torch.bfloat16, 4)
+    """Decode attention over a padded cache [B,Hkv,cap,D] (bf16, or fp16
+    through ``attn_decode_padded_f16``), with L_b = min(seqlens[b], cap);
+    otherwise as ``attn_decode``.  ``rope_base`` > 0 rotates each query to
+    its position L_b - 1 in the kernel."""
+    name = _fn("attn_decode_padded", q.dtype)
+    _check(q, "q", q.dtype, 3)
+    _check(kcache, "kcache", q.dtype, 4)
+    _check(vcache, "vcache", q.dtype, 4)
     _check(seqlens, "seqlens", torch.int32, 1)
     B, Hq, D = q.shape
     Hkv, cap = kcache.shape[1], kcache.shape[2]
-    if kcache.shape != (B, Hkv, cap, D) or vcache.shape != kcache.shape:
-        raise ValueError("kcache, vcache must be [B,Hkv,cap,D]")
+    _shape(kcache, "kcache", (B, Hkv, cap, D))
+    _shape(vcache, "vcache", kcache.shape)
+    _shape(seqlens, "seqlens", (B,))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    _check(out, "out", torch.bfloat16, 3)
-    if with_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 2)
-    if workspace is None:
-        workspace = new_decode_workspace(B, Hq, Hkv, D, num_splits, q.device)
-    _check(workspace, "workspace", torch.uint8, 1)
-    st = lib().attn_decode_padded(
+    out, lse, workspace = _decode_outputs(q, out, lse, with_lse, workspace,
+                                          Hkv, num_splits)
+    _on_gpu(q=q, kcache=kcache, vcache=vcache, seqlens=seqlens, out=out,
+            lse=lse, workspace=workspace)
+    st = getattr(lib(), name)(
         _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B, Hq,
         Hkv, D, cap, float(scale), int(num_splits), _ptr(lse),
         float(rope_base), _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
-        raise AttnError(st, "attn_decode_padded")
+        raise AttnError(st, name)
     return out, lse
 
 
@@ -406,23 +439,18 @@ class PreparedCall:
 
 
 def prepare_prefill(q, k, v, out, lse=None, causal=True, scale=None):
-    """A PreparedCall of attn_prefill / attn_prefill_f32 on the current
-    stream (arguments as for ``attn_prefill``; ``out`` is required)."""
+    """A PreparedCall of attn_prefill / _f16 / _f32 on the current stream
+    (arguments as for ``attn_prefill``; ``out`` is required)."""
     dtype = q.dtype
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
-        _check(t, n, dtype, 4)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or out.shape != q.shape:
-        raise ValueError("inconsistent prefill shapes")
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 3)
-        if lse.shape != (B, Hq, S):
-            raise ValueError("lse must be [B,Hq,S]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     if dtype not in _PREFILL_FN:
         raise ValueError("q must be bfloat16, float16 or float32")
+    B, Hq, Hkv, S, D = _prefill_shapes(q, k, v, dtype)
+    _check(out, "out", dtype, 4)
+    _shape(out, "out", q.shape)
+    lse = _lse_arg(lse, False, (B, Hq, S), q)
+    _on_gpu(q=q, k=k, v=v, out=out, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
     fn = getattr(lib(), _PREFILL_FN[dtype])
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
             D, ctypes.c_float(scale), int(bool(causal)), _stream())
@@ -441,11 +469,16 @@ def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
     _check(kcache, "kcache", dtype, None)
     _check(vcache, "vcache", dtype, None)
     _check(seqlens, "seqlens", torch.int32, 1)
-    _check(out, "out", dtype, 3)
-    _check(workspace, "workspace", torch.uint8, 1)
-    if lse is not None:
-        _check(lse, "lse", torch.float32, 2)
     B, Hq, D = q.shape
+    _shape(seqlens, "seqlens", (B,))
+    if kcache.numel() != vcache.numel():
+        raise ValueError("kcache and vcache must have the same size")
+    _check(out, "out", dtype, 3)
+    _shape(out, "out", q.shape)
+    _check(workspace, "workspace", torch.uint8, 1)
+    lse = _lse_arg(lse, False, (B, Hq), q)
+    _on_gpu(q=q, kcache=kcache, vcache=vcache, seqlens=seqlens, out=out,
+            lse=lse, workspace=workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     args = (_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B,
@@ -454,3 +487,9 @@ def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
     return PreparedCall(getattr(lib(), _DECODE_FN[dtype]), _DECODE_FN[dtype],
                         args, (q, kcache, vcache, seqlens, out, workspace,
                                lse))
+
+
+def prefill_workgroups(B, Hq, S, D):
+    """Workgroups one prefill launch uses: one per (batch, query head,
+    128-row query tile)."""
+    return B * Hq * -(-S // 128)

@@ -14,7 +14,6 @@
 
 namespace {
 
-using attn::kDecodeThreads;
 using attn::kPrefillBM;
 using attn::kPrefillThreads;
 
@@ -289,6 +288,121 @@ int decode16(const void* q, const void* kcache, const void* vcache,
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// Prefill with RoPE: K rotated once into k_rot by a first launch (every
+// query tile of its head reads it), q rotated on load by the attention
+// kernel.
+template <typename T>
+int prefill_rope16(const void* q, const void* k, const void* v, void* o,
+                   float* lse, void* k_rot, int B, int Hq, int Hkv, int S,
+                   int D, float scale, int causal, float rope_base,
+                   void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK) return st;
+  if (!rope_base_ok(rope_base) || !(rope_base > 0.f)) return ATTN_ERR_SCALE;
+  if (empty) return ATTN_OK;
+  if (!k_rot) return ATTN_ERR_NULL;
+  if (!aligned(k_rot, 16)) return ATTN_ERR_ALIGN;
+  const attn::RopeRates rope = rope_rates(rope_base, D);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const long long rows = (long long)B * Hkv * S;
+  const long long threads = rows * (D / 16);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const T* kb = static_cast<const T*>(k);
+  T* kr = static_cast<T*>(k_rot);
+  if (D == 64)
+    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<T, 64>), grid, dim3(256),
+                       0, hs, kb, kr, rows, S, rope);
+  else
+    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<T, 128>), grid, dim3(256),
+                       0, hs, kb, kr, rows, S, rope);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  return launch_prefill<T, Half16Prefill<T>::template L>(
+      static_cast<const T*>(q), kr, static_cast<const T*>(v),
+      static_cast<T*>(o), lse, B, Hq, Hkv, S, D, scale, causal, stream, 1,
+      rope);
+}
+
+template <typename T>
+int prefill_varlen16(const void* q, const void* k, const void* v, void* o,
+                     float* lse, const int* cu_seqlens, int B, int max_seqlen,
+                     int Hq, int Hkv, int D, float scale, int causal,
+                     void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, max_seqlen, D,
+                               scale, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!cu_seqlens) return ATTN_ERR_NULL;
+  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
+  return launch_prefill<T, Half16Prefill<T>::template L>(
+      static_cast<const T*>(q), static_cast<const T*>(k),
+      static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv,
+      max_seqlen, D, scale, causal, stream, 0, attn::RopeRates{}, cu_seqlens);
+}
+
+template <typename T>
+int prefill_padded16(const void* q, const void* k, const void* v, void* o,
+                     float* lse, const int* seqlens, int B, int Hq, int Hkv,
+                     int S, int D, float scale, int causal, void* stream) {
+  bool empty;
+  const int st =
+      check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!seqlens) return ATTN_ERR_NULL;
+  if (!aligned(seqlens, 4)) return ATTN_ERR_ALIGN;
+  return launch_prefill<T, Half16Prefill<T>::template L>(
+      static_cast<const T*>(q), static_cast<const T*>(k),
+      static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv, S, D,
+      scale, causal, stream, 0, attn::RopeRates{}, nullptr, seqlens);
+}
+
+template <typename T>
+int decode_padded16(const void* q, const void* kcache, const void* vcache,
+                    const int* seqlens, void* o, int B, int Hq, int Hkv, int D,
+                    int cap, float scale, int num_splits, float* lse,
+                    float rope_base, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (cap <= 0) return B == 0 ? ATTN_OK : ATTN_ERR_SHAPE;
+  if ((long long)B * Hkv * cap > 0x7fffffffffffLL) return ATTN_ERR_SHAPE;
+  return decode16<T>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, cap, scale,
+                     num_splits, lse, workspace, workspace_bytes, stream,
+                     rope_base);
+}
+
+// KV-cache append for element type T (the RoPE rotation reads and writes T).
+template <typename T>
+int kv_append16(const void* k_new, const void* v_new, void* kcache,
+                void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
+                float rope_base, void* stream) {
+  if (B < 0 || Hkv < 0 || cap < 0) return ATTN_ERR_SHAPE;
+  if (!rope_base_ok(rope_base)) return ATTN_ERR_SCALE;
+  const attn::RopeRates rope = rope_rates(rope_base, D);
+  const int use_rope = rope_base > 0.f;
+  if (Hkv == 0) return ATTN_ERR_GQA;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (B == 0) return ATTN_OK;
+  if (cap == 0) return ATTN_ERR_SHAPE;
+  if (!k_new || !v_new || !kcache || !vcache || !seqlens) return ATTN_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kcache, 16) ||
+      !aligned(vcache, 16) || !aligned(seqlens, 4))
+    return ATTN_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const T* kn = static_cast<const T*>(k_new);
+  const T* vn = static_cast<const T*>(v_new);
+  T* kc = static_cast<T*>(kcache);
+  T* vc = static_cast<T*>(vcache);
+  if (D == 64)
+    hipLaunchKernelGGL((attn::attn_kv_append_kernel<T, 64>), dim3(B),
+                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
+                       seqlens, Hkv, cap, use_rope, rope);
+  else
+    hipLaunchKernelGGL((attn::attn_kv_append_kernel<T, 128>), dim3(B),
+                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
+                       seqlens, Hkv, cap, use_rope, rope);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,66 +425,49 @@ int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
                       float* lse, void* k_rot, int B, int Hq, int Hkv, int S,
                       int D, float scale, int causal, float rope_base,
                       void* stream) {
-  bool empty;
-  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
-                               &empty);
-  if (st != ATTN_OK) return st;
-  if (!rope_base_ok(rope_base) || !(rope_base > 0.f)) return ATTN_ERR_SCALE;
-  if (empty) return ATTN_OK;
-  if (!k_rot) return ATTN_ERR_NULL;
-  if (!aligned(k_rot, 16)) return ATTN_ERR_ALIGN;
-  const attn::RopeRates rope = rope_rates(rope_base, D);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  // K rotated once (every query tile of its head reads it), into k_rot
-  const long long rows = (long long)B * Hkv * S;
-  const long long threads = rows * (D / 16);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  const __bf16* kb = static_cast<const __bf16*>(k);
-  __bf16* kr = static_cast<__bf16*>(k_rot);
-  if (D == 64)
-    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<__bf16, 64>), grid,
-                       dim3(256), 0, hs, kb, kr, rows, S, rope);
-  else
-    hipLaunchKernelGGL((attn::attn_rope_rows_kernel<__bf16, 128>), grid,
-                       dim3(256), 0, hs, kb, kr, rows, S, rope);
-  if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
-  // Q rotated on load inside the attention kernel
-  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
-      static_cast<const __bf16*>(q), kr, static_cast<const __bf16*>(v),
-      static_cast<__bf16*>(o), lse, B, Hq, Hkv, S, D, scale, causal, stream,
-      1, rope);
+  return prefill_rope16<__bf16>(q, k, v, o, lse, k_rot, B, Hq, Hkv, S, D,
+                                scale, causal, rope_base, stream);
+}
+
+int attn_prefill_rope_f16(const void* q, const void* k, const void* v,
+                          void* o, float* lse, void* k_rot, int B, int Hq,
+                          int Hkv, int S, int D, float scale, int causal,
+                          float rope_base, void* stream) {
+  return prefill_rope16<_Float16>(q, k, v, o, lse, k_rot, B, Hq, Hkv, S, D,
+                                  scale, causal, rope_base, stream);
 }
 
 int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                         float* lse, const int* cu_seqlens, int B,
                         int max_seqlen, int Hq, int Hkv, int D, float scale,
                         int causal, void* stream) {
-  bool empty;
-  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, max_seqlen, D,
-                               scale, &empty);
-  if (st != ATTN_OK || empty) return st;
-  if (!cu_seqlens) return ATTN_ERR_NULL;
-  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_ALIGN;
-  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
-      max_seqlen, D, scale, causal, stream, 0, attn::RopeRates{}, cu_seqlens);
+  return prefill_varlen16<__bf16>(q, k, v, o, lse, cu_seqlens, B, max_seqlen,
+                                  Hq, Hkv, D, scale, causal, stream);
+}
+
+int attn_prefill_varlen_f16(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const int* cu_seqlens, int B,
+                            int max_seqlen, int Hq, int Hkv, int D,
+                            float scale, int causal, void* stream) {
+  return prefill_varlen16<_Float16>(q, k, v, o, lse, cu_seqlens, B,
+                                    max_seqlen, Hq, Hkv, D, scale, causal,
+                                    stream);
 }
 
 int attn_prefill_padded(const void* q, const void* k, const void* v, void* o,
                         float* lse, const int* seqlens, int B, int Hq,
                         int Hkv, int S, int D, float scale, int causal,
                         void* stream) {
-  bool empty;
-  const int st =
-      check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, &empty);
-  if (st != ATTN_OK || empty) return st;
-  if (!seqlens) return ATTN_ERR_NULL;
-  if (!aligned(seqlens, 4)) return ATTN_ERR_ALIGN;
-  return launch_prefill<__bf16, Half16Prefill<__bf16>::template L>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, Hq, Hkv,
-      S, D, scale, causal, stream, 0, attn::RopeRates{}, nullptr, seqlens);
+  return prefill_padded16<__bf16>(q, k, v, o, lse, seqlens, B, Hq, Hkv, S, D,
+                                  scale, causal, stream);
+}
+
+int attn_prefill_padded_f16(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const int* seqlens, int B,
+                            int Hq, int Hkv, int S, int D, float scale,
+                            int causal, void* stream) {
+  return prefill_padded16<_Float16>(q, k, v, o, lse, seqlens, B, Hq, Hkv, S,
+                                    D, scale, causal, stream);
 }
 
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
@@ -416,42 +513,34 @@ int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
                        int D, int cap, float scale, int num_splits, float* lse,
                        float rope_base, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  if (cap <= 0) return B == 0 ? ATTN_OK : ATTN_ERR_SHAPE;
-  if ((long long)B * Hkv * cap > 0x7fffffffffffLL) return ATTN_ERR_SHAPE;
-  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, cap,
-                          scale, num_splits, lse, workspace, workspace_bytes,
-                          stream, rope_base);
+  return decode_padded16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D,
+                                 cap, scale, num_splits, lse, rope_base,
+                                 workspace, workspace_bytes, stream);
+}
+
+int attn_decode_padded_f16(const void* q, const void* kcache,
+                           const void* vcache, const int* seqlens, void* o,
+                           int B, int Hq, int Hkv, int D, int cap, float scale,
+                           int num_splits, float* lse, float rope_base,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode_padded16<_Float16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv,
+                                   D, cap, scale, num_splits, lse, rope_base,
+                                   workspace, workspace_bytes, stream);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
                    void* vcache, int* seqlens, int B, int Hkv, int D, int cap,
                    float rope_base, void* stream) {
-  if (B < 0 || Hkv < 0 || cap < 0) return ATTN_ERR_SHAPE;
-  if (!rope_base_ok(rope_base)) return ATTN_ERR_SCALE;
-  const attn::RopeRates rope = rope_rates(rope_base, D);
-  const int use_rope = rope_base > 0.f;
-  if (Hkv == 0) return ATTN_ERR_GQA;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (B == 0) return ATTN_OK;
-  if (cap == 0) return ATTN_ERR_SHAPE;
-  if (!k_new || !v_new || !kcache || !vcache || !seqlens) return ATTN_ERR_NULL;
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kcache, 16) ||
-      !aligned(vcache, 16) || !aligned(seqlens, 4))
-    return ATTN_ERR_ALIGN;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const __bf16* kn = static_cast<const __bf16*>(k_new);
-  const __bf16* vn = static_cast<const __bf16*>(v_new);
-  __bf16* kc = static_cast<__bf16*>(kcache);
-  __bf16* vc = static_cast<__bf16*>(vcache);
-  if (D == 64)
-    hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 64>), dim3(B),
-                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
-                       seqlens, Hkv, cap, use_rope, rope);
-  else
-    hipLaunchKernelGGL((attn::attn_kv_append_kernel<__bf16, 128>), dim3(B),
-                       dim3(attn::kAppendThreads), 0, hs, kn, vn, kc, vc,
-                       seqlens, Hkv, cap, use_rope, rope);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return kv_append16<__bf16>(k_new, v_new, kcache, vcache, seqlens, B, Hkv, D,
+                             cap, rope_base, stream);
+}
+
+int attn_kv_append_f16(const void* k_new, const void* v_new, void* kcache,
+                       void* vcache, int* seqlens, int B, int Hkv, int D,
+                       int cap, float rope_base, void* stream) {
+  return kv_append16<_Float16>(k_new, v_new, kcache, vcache, seqlens, B, Hkv,
+                               D, cap, rope_base, stream);
 }
 
 const char* attn_status_string(int status) {

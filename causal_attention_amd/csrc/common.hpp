@@ -7,8 +7,6 @@
 
 namespace attn {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -20,14 +18,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Lazy rescaling of the online softmax: the running output is rescaled only
 // when a row max exceeds the reference by more than this many log2 units.
 constexpr float kLazyRescale = 8.f;
-
-// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.  Lane l holds
-// row (A) / column (B) l % 32 and eight contraction elements; C lane l holds
-// column l % 32, rows 8*(i/4) + 4*(l/32) + i%4 for i in 0..15.
-__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b,
-                                                     f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // 16-bit input elements: bf16 (the workloads' type) and fp16.  The kernels
 // are written once against these traits: the 8-element MFMA operand vector,
@@ -101,43 +91,6 @@ __device__ __forceinline__ float fast_exp2(float x) {
 
 __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
-}
-
-// bf16 bits -> fp32 (exact).
-__device__ __forceinline__ float bf16_lo(uint32_t w) {
-  return __uint_as_float(w << 16);
-}
-__device__ __forceinline__ float bf16_hi(uint32_t w) {
-  return __uint_as_float(w & 0xffff0000u);
-}
-
-// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Cross-lane moves inside rows of 16 lanes (DPP; no LDS traffic).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(
-      0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
-constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
-
-// Sum over aligned groups of N lanes (N = 8 or 16); every lane gets the sum.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
-  x += dpp<kDppXor1>(x);
-  x += dpp<kDppXor2>(x);
-  x += dpp<kDppHalfMirror>(x);
-  if constexpr (N == 16) x += dpp<kDppMirror>(x);
-  return x;
 }
 
 // Exchange with the lane 32 positions away (the other half of the wave).

@@ -46,8 +46,6 @@
 
 namespace attn {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kDecodeBlock = 32;                  // keys per block
 
 

@@ -111,6 +111,16 @@ int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
                       void* stream);
 
 /*
+ * attn_prefill_rope with fp16 storage: q, k, v, o and k_rot in IEEE fp16
+ * (fp32 rotation and accumulation, as for attn_prefill_f16).  Same
+ * arguments, layouts and errors.
+ */
+int attn_prefill_rope_f16(const void* q, const void* k, const void* v,
+                          void* o, float* lse, void* k_rot, int B, int Hq,
+                          int Hkv, int S, int D, float scale, int causal,
+                          float rope_base, void* stream);
+
+/*
  * Prefill attention over a ragged batch (variable sequence lengths), bf16:
  * the padding mask of the attention-fusion page, section 4.3, and the
  * dynamic shapes of its section 6.1, with no padding stored at all.
@@ -132,6 +142,15 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                         int causal, void* stream);
 
 /*
+ * attn_prefill_varlen with fp16 storage (q, k, v, o in IEEE fp16).  Same
+ * arguments, layouts and errors.
+ */
+int attn_prefill_varlen_f16(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const int* cu_seqlens, int B,
+                            int max_seqlen, int Hq, int Hkv, int D,
+                            float scale, int causal, void* stream);
+
+/*
  * Prefill attention over a padded batch, bf16: the padding mask of the
  * attention-fusion page, section 4.3, on the dense layout of attn_prefill
  * (every sequence stored with S rows, the first L_b of them valid).
@@ -148,6 +167,15 @@ int attn_prefill_padded(const void* q, const void* k, const void* v, void* o,
                         float* lse, const int* seqlens, int B, int Hq,
                         int Hkv, int S, int D, float scale, int causal,
                         void* stream);
+
+/*
+ * attn_prefill_padded with fp16 storage (q, k, v, o in IEEE fp16).  Same
+ * arguments, layouts and errors.
+ */
+int attn_prefill_padded_f16(const void* q, const void* k, const void* v,
+                            void* o, float* lse, const int* seqlens, int B,
+                            int Hq, int Hkv, int S, int D, float scale,
+                            int causal, void* stream);
 
 /*
  * Prefill attention, fp32 storage.  Same arguments and layouts as
@@ -224,9 +252,9 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
  * Qwen3.5-0.8B page ("手写Triton kernel重构Qwen3.5-0.8B", section 2.2, row 18:
  * write the new k/v into the KV cache), shaped for the CUDA Graph decode of
  * that page's section 4 (preallocated buffers, positions on the device).
- *   k_new, v_new  : [B, Hkv, D] 16-bit elements (bf16 or fp16; copied bit for
- *                   bit), 16-byte aligned
- *   kcache, vcache: [B, Hkv, cap, D] of the same type, the "padded" cache:
+ *   k_new, v_new  : [B, Hkv, D] bf16, 16-byte aligned (v is copied bit for
+ *                   bit; k too unless it is rotated)
+ *   kcache, vcache: [B, Hkv, cap, D] bf16, the "padded" cache:
  *                   sequence b holds seqlens[b] valid rows per KV head
  *   seqlens       : DEVICE int32 [B].  For every b with
  *                   0 <= seqlens[b] < cap, row seqlens[b] of each KV head of
@@ -246,6 +274,15 @@ int attn_kv_append(const void* k_new, const void* v_new, void* kcache,
                    float rope_base, void* stream);
 
 /*
+ * attn_kv_append for fp16 caches: k_new, v_new [B, Hkv, D] and kcache,
+ * vcache [B, Hkv, cap, D] in IEEE fp16 (a rotated k is computed in fp32 and
+ * rounded to fp16).  Same arguments and errors.
+ */
+int attn_kv_append_f16(const void* k_new, const void* v_new, void* kcache,
+                       void* vcache, int* seqlens, int B, int Hkv, int D,
+                       int cap, float rope_base, void* stream);
+
+/*
  * Decode attention over the padded cache of attn_kv_append: attn_decode with
  * kcache, vcache [B, Hkv, cap, D] bf16 and L_b = min(seqlens[b], cap).  Same
  * q, o, lse, num_splits, workspace (attn_decode_workspace_size) and errors;
@@ -261,6 +298,17 @@ int attn_decode_padded(const void* q, const void* kcache, const void* vcache,
                        int D, int cap, float scale, int num_splits, float* lse,
                        float rope_base, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_padded for fp16 caches (the ones attn_kv_append_f16 fills):
+ * q, o, kcache, vcache in IEEE fp16.  Same arguments, workspace and errors.
+ */
+int attn_decode_padded_f16(const void* q, const void* kcache,
+                           const void* vcache, const int* seqlens, void* o,
+                           int B, int Hq, int Hkv, int D, int cap, float scale,
+                           int num_splits, float* lse, float rope_base,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* A static description of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);

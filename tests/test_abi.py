@@ -27,6 +27,9 @@ def test_header_declares_the_entry_points():
               "attn_prefill_rope", "attn_prefill_varlen",
               "attn_prefill_padded", "attn_decode",
               "attn_decode_f16", "attn_decode_padded", "attn_kv_append",
+              "attn_prefill_rope_f16", "attn_prefill_varlen_f16",
+              "attn_prefill_padded_f16", "attn_kv_append_f16",
+              "attn_decode_padded_f16",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
               "attn_status_string"]:
         assert n in names
@@ -108,12 +111,17 @@ def test_decode_argument_errors(fn):
 
 
 def padded(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, cap=64,
-           scale=0.1, ns=0, lse=None, rope=0.0, ws=A, wsb=1 << 30):
-    return attn.lib().attn_decode_padded(q, kc, vc, sl, o, B, Hq, Hkv, D, cap,
-                                         scale, ns, lse, rope, ws, wsb, None)
+           scale=0.1, ns=0, lse=None, rope=0.0, ws=A, wsb=1 << 30,
+           fn="attn_decode_padded"):
+    return getattr(attn.lib(), fn)(q, kc, vc, sl, o, B, Hq, Hkv, D, cap,
+                                   scale, ns, lse, rope, ws, wsb, None)
 
 
-def test_decode_padded_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_decode_padded",
+                                "attn_decode_padded_f16"])
+def test_decode_padded_argument_errors(fn):
+    import functools
+    padded = functools.partial(globals()["padded"], fn=fn)
     assert padded(cap=0) == -2
     assert padded(cap=-3) == -2
     assert padded(B=0, cap=0) == 0
@@ -126,12 +134,16 @@ def test_decode_padded_argument_errors():
     assert padded(rope=float("inf")) == -9
 
 
-def append(kn=A, vn=A, kc=A, vc=A, sl=A, B=4, Hkv=2, D=128, cap=64, rope=0.0):
-    return attn.lib().attn_kv_append(kn, vn, kc, vc, sl, B, Hkv, D, cap, rope,
-                                     None)
+def append(kn=A, vn=A, kc=A, vc=A, sl=A, B=4, Hkv=2, D=128, cap=64, rope=0.0,
+           fn="attn_kv_append"):
+    return getattr(attn.lib(), fn)(kn, vn, kc, vc, sl, B, Hkv, D, cap, rope,
+                                   None)
 
 
-def test_kv_append_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_kv_append", "attn_kv_append_f16"])
+def test_kv_append_argument_errors(fn):
+    import functools
+    append = functools.partial(globals()["append"], fn=fn)
     assert append(B=-1) == -2
     assert append(cap=-1) == -2
     assert append(cap=0) == -2
@@ -147,12 +159,16 @@ def test_kv_append_argument_errors():
 
 
 def prefill_rope(q=A, k=A, v=A, o=A, lse=A, kr=A, B=1, Hq=8, Hkv=2, S=64,
-                 D=128, scale=0.1, causal=1, rope=10000.0):
-    return attn.lib().attn_prefill_rope(q, k, v, o, lse, kr, B, Hq, Hkv, S, D,
-                                        scale, causal, rope, None)
+                 D=128, scale=0.1, causal=1, rope=10000.0,
+                 fn="attn_prefill_rope"):
+    return getattr(attn.lib(), fn)(q, k, v, o, lse, kr, B, Hq, Hkv, S, D,
+                                   scale, causal, rope, None)
 
 
-def test_prefill_rope_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_prefill_rope", "attn_prefill_rope_f16"])
+def test_prefill_rope_argument_errors(fn):
+    import functools
+    prefill_rope = functools.partial(globals()["prefill_rope"], fn=fn)
     assert prefill_rope(kr=None) == -1
     assert prefill_rope(kr=A + 8) == -5
     assert prefill_rope(rope=0.0) == -9
@@ -165,12 +181,16 @@ def test_prefill_rope_argument_errors():
 
 
 def varlen(q=A, k=A, v=A, o=A, lse=A, cu=A, B=3, maxs=100, Hq=8, Hkv=2,
-           D=128, scale=0.1, causal=1):
-    return attn.lib().attn_prefill_varlen(q, k, v, o, lse, cu, B, maxs, Hq,
-                                          Hkv, D, scale, causal, None)
+           D=128, scale=0.1, causal=1, fn="attn_prefill_varlen"):
+    return getattr(attn.lib(), fn)(q, k, v, o, lse, cu, B, maxs, Hq, Hkv, D,
+                                   scale, causal, None)
 
 
-def test_prefill_varlen_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_prefill_varlen",
+                                "attn_prefill_varlen_f16"])
+def test_prefill_varlen_argument_errors(fn):
+    import functools
+    varlen = functools.partial(globals()["varlen"], fn=fn)
     assert varlen(cu=None) == -1
     assert varlen(cu=A + 2) == -5
     assert varlen(q=None) == -1
@@ -183,12 +203,16 @@ def test_prefill_varlen_argument_errors():
 
 
 def prefill_padded(q=A, k=A, v=A, o=A, lse=A, sl=A, B=3, Hq=8, Hkv=2, S=100,
-                   D=128, scale=0.1, causal=1):
-    return attn.lib().attn_prefill_padded(q, k, v, o, lse, sl, B, Hq, Hkv, S,
-                                          D, scale, causal, None)
+                   D=128, scale=0.1, causal=1, fn="attn_prefill_padded"):
+    return getattr(attn.lib(), fn)(q, k, v, o, lse, sl, B, Hq, Hkv, S, D,
+                                   scale, causal, None)
 
 
-def test_prefill_padded_argument_errors():
+@pytest.mark.parametrize("fn", ["attn_prefill_padded",
+                                "attn_prefill_padded_f16"])
+def test_prefill_padded_argument_errors(fn):
+    import functools
+    prefill_padded = functools.partial(globals()["prefill_padded"], fn=fn)
     assert prefill_padded(sl=None) == -1
     assert prefill_padded(sl=A + 2) == -5
     assert prefill_padded(q=None) == -1
@@ -258,3 +282,84 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_prefill(x, x, x)
+
+
+# ------------------------------------------- binding checks (host tensors)
+#
+# The binding checks every shape before it checks devices, so host tensors
+# of a wrong shape are refused with a shape error here, and host tensors of
+# the right shapes reach the device check (no GPU call is made either way).
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def _raises(match, fn, *a, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_binding_checks_prefill_output_shapes():
+    import torch
+    q, k = _t(1, 8, 64, 128), _t(1, 2, 64, 128)
+    _raises("out must have shape", attn.attn_prefill, q, k, k,
+            out=_t(1, 8, 32, 128))
+    _raises("lse must have shape", attn.attn_prefill, q, k, k,
+            lse=_t(1, 8, 32, dtype=torch.float32))
+    _raises("GPU tensor", attn.attn_prefill, q, k, k)
+    _raises("k_rot must have shape", attn.attn_prefill_rope, q, k, k, 1e4,
+            k_rot=_t(1, 2, 32, 128))
+    _raises("out must have shape", attn.attn_prefill_rope, q, k, k, 1e4,
+            out=_t(1, 8, 64, 64))
+    _raises("lse must have shape", attn.attn_prefill_rope, q, k, k, 1e4,
+            lse=_t(1, 8, 32, dtype=torch.float32))
+    sl = torch.zeros(1, dtype=torch.int32)
+    _raises("out must have shape", attn.attn_prefill_padded, q, k, k, sl,
+            out=_t(1, 8, 63, 128))
+    _raises("seqlens must have shape", attn.attn_prefill_padded, q, k, k,
+            torch.zeros(2, dtype=torch.int32))
+    _raises("bfloat16 or float16", attn.attn_prefill_rope,
+            q.float(), k.float(), k.float(), 1e4)
+
+
+def test_binding_checks_decode_output_shapes():
+    import torch
+    q, kc = _t(4, 8, 128), _t(4 * 2 * 10 * 128)
+    sl = torch.zeros(4, dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    _raises("out must have shape", attn.attn_decode, q, kc, kc, sl, 2,
+            out=_t(4, 4, 128), workspace=ws)
+    _raises("lse must have shape", attn.attn_decode, q, kc, kc, sl, 2,
+            lse=_t(4, 4, dtype=torch.float32), workspace=ws)
+    _raises("seqlens must have shape", attn.attn_decode, q, kc, kc,
+            torch.zeros(3, dtype=torch.int32), 2, workspace=ws)
+    _raises("GPU tensor", attn.attn_decode, q, kc, kc, sl, 2, workspace=ws)
+    pc = _t(4, 2, 10, 128)
+    _raises("out must have shape", attn.attn_decode_padded, q, pc, pc, sl,
+            out=_t(4, 8, 64), workspace=ws)
+    _raises("lse must have shape", attn.attn_decode_padded, q, pc, pc, sl,
+            lse=_t(4, 4, dtype=torch.float32), workspace=ws)
+    _raises("out must have shape", attn.prepare_decode, q, kc, kc, sl,
+            _t(4, 8, 64), 2, ws)
+    _raises("lse must have shape", attn.prepare_decode, q, kc, kc, sl,
+            _t(4, 8, 128), 2, ws, lse=_t(4, 4, dtype=torch.float32))
+    _raises("out must have shape", attn.prepare_prefill, _t(1, 8, 64, 128),
+            _t(1, 2, 64, 128), _t(1, 2, 64, 128), _t(1, 8, 64, 64))
+
+
+def test_binding_checks_append_shapes_and_types():
+    import torch
+    kc = _t(4, 2, 10, 128)
+    sl = torch.zeros(4, dtype=torch.int32)
+    _raises("k_new must have shape", attn.attn_kv_append, _t(4, 2, 64),
+            _t(4, 2, 128), kc, kc, sl)
+    _raises("vcache must have shape", attn.attn_kv_append, _t(4, 2, 128),
+            _t(4, 2, 128), kc, _t(4, 2, 9, 128), sl)
+    _raises("must be torch.float16", attn.attn_kv_append,
+            _t(4, 2, 128, dtype=torch.float16), _t(4, 2, 128), kc, kc, sl)
+    _raises("bfloat16 or float16", attn.attn_kv_append,
+            _t(4, 2, 128, dtype=torch.float32),
+            _t(4, 2, 128, dtype=torch.float32), kc.float(), kc.float(), sl)
+    _raises("GPU tensor", attn.attn_kv_append, _t(4, 2, 128), _t(4, 2, 128),
+            kc, kc, sl)
