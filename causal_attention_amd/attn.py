@@ -23,6 +23,7 @@ STATUS = {
     -9: "ATTN_ERR_SCALE",
 }
 MAX_SPLITS = 4096
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class AttnError(ValueError):
@@ -72,6 +73,9 @@ def lib():
         L.attn_prefill_padded.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
                                           i, f, i, vp]
         L.attn_prefill_padded.restype = i
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f,
+                                          i, vp, vp]
+        L.attn_decode_noalloc.restype = i
         for n in ("attn_prefill_rope_f16", "attn_prefill_varlen_f16",
                   "attn_prefill_padded_f16", "attn_kv_append_f16",
                   "attn_decode_padded_f16"):
@@ -248,6 +252,38 @@ def attn_decode(q, kcache, vcache, seqlens, Hkv, num_splits=0, scale=None,
             _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise AttnError(st, _DECODE_FN[dtype])
+    return out, lse
+
+
+def attn_decode_noalloc(q, kcache, vcache, seqlens, Hkv, out, num_splits=0,
+                        scale=None, lse=None):
+    """``attn_decode`` (bf16) without a workspace argument: the library's
+    fixed device-resident workspace is used (see ``attn_decode_noalloc`` in
+    attn.h).  ``out`` (and ``lse`` if wanted) are required, so the call
+    allocates nothing.  Returns (out, lse)."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(kcache, "kcache", torch.bfloat16, None)
+    _check(vcache, "vcache", torch.bfloat16, None)
+    _check(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, D = q.shape
+    _shape(seqlens, "seqlens", (B,))
+    if kcache.numel() != vcache.numel():
+        raise ValueError("kcache and vcache must have the same size")
+    _check(out, "out", torch.bfloat16, 3)
+    _shape(out, "out", q.shape)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+        _shape(lse, "lse", (B, Hq))
+    _on_gpu(q=q, kcache=kcache, vcache=vcache, seqlens=seqlens, out=out,
+            lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib().attn_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache),
+                                   _ptr(seqlens), _ptr(out), B, Hq, Hkv, D,
+                                   float(scale), int(num_splits), _ptr(lse),
+                                   _stream())
+    if st != 0:
+        raise AttnError(st, "attn_decode_noalloc")
     return out, lse
 
 

@@ -403,6 +403,33 @@ int kv_append16(const void* k_new, const void* v_new, void* kcache,
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// ------------------------------------------------- no-allocation decode
+//
+// The decode workspace of attn_decode_noalloc: a fixed array in device
+// memory, one copy per GPU, held until the process ends.  In host code the
+// name `scratch` stands for the symbol, not for a device address: every use
+// goes through the address hipGetSymbolAddress returns for the current
+// device, taken once per device and kept.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device (nullptr when the
+// lookup fails).  Concurrent first calls may both look it up and store the
+// same address.
+void* scratch_address() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess)
+      return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,6 +533,21 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
   return decode16<_Float16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, 0,
                             scale, num_splits, lse, workspace, workspace_bytes,
                             stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* kcache,
+                        const void* vcache, const int* seqlens, void* o, int B,
+                        int Hq, int Hkv, int D, float scale, int num_splits,
+                        float* lse, void* stream) {
+  const int st = check_decode_sizes(B, Hq, Hkv, D, num_splits);
+  if (st != ATTN_OK) return st;
+  const int P = num_splits == 0 ? auto_splits(B, Hkv) : num_splits;
+  if (B > 0 && decode_workspace(B, Hq, Hkv, D, P).bytes > kScratchBytes)
+    return ATTN_ERR_WORKSPACE;
+  void* ws = B > 0 ? scratch_address() : nullptr;
+  if (B > 0 && ws == nullptr) return ATTN_ERR_LAUNCH;
+  return decode16<__bf16>(q, kcache, vcache, seqlens, o, B, Hq, Hkv, D, 0,
+                          scale, num_splits, lse, ws, kScratchBytes, stream);
 }
 
 int attn_decode_padded(const void* q, const void* kcache, const void* vcache,

@@ -247,6 +247,34 @@ int attn_decode_f16(const void* q, const void* kcache, const void* vcache,
                     float scale, int num_splits, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Size of the device-resident workspace of attn_decode_noalloc (8 MiB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * attn_decode without a caller workspace, for callers that cannot allocate
+ * device memory or pass scratch (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same q, kcache, vcache,
+ * seqlens, o, sizes, scale, num_splits, lse and stream as attn_decode, and
+ * the same kernels and results.  The workspace is a fixed
+ * ATTN_NOALLOC_SCRATCH_BYTES array in device memory that the library holds
+ * on each GPU it runs on until the process ends; the library looks up its
+ * address once per device, on the first call made with that device current
+ * (the stream must belong to the current device).  No call allocates or
+ * frees memory.
+ * Errors: as attn_decode, plus ATTN_ERR_WORKSPACE when
+ * attn_decode_workspace_size(B, Hq, Hkv, D, num_splits) exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES, and ATTN_ERR_LAUNCH when the array's address
+ * cannot be obtained.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap in
+ * time on the same GPU (different streams, or host threads) race on it and
+ * must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls (its contents on entry do not matter).
+ */
+int attn_decode_noalloc(const void* q, const void* kcache,
+                        const void* vcache, const int* seqlens, void* o, int B,
+                        int Hq, int Hkv, int D, float scale, int num_splits,
+                        float* lse, void* stream);
+
 /*
  * KV-cache append: the kv_cache_store step of the operator table of the
  * Qwen3.5-0.8B page ("手写Triton kernel重构Qwen3.5-0.8B", section 2.2, row 18:

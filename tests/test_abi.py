@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
               "attn_decode_f16", "attn_decode_padded", "attn_kv_append",
               "attn_prefill_rope_f16", "attn_prefill_varlen_f16",
               "attn_prefill_padded_f16", "attn_kv_append_f16",
-              "attn_decode_padded_f16",
+              "attn_decode_padded_f16", "attn_decode_noalloc",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
               "attn_status_string"]:
         assert n in names
@@ -363,3 +363,24 @@ def test_binding_checks_append_shapes_and_types():
             _t(4, 2, 128, dtype=torch.float32), kc.float(), kc.float(), sl)
     _raises("GPU tensor", attn.attn_kv_append, _t(4, 2, 128), _t(4, 2, 128),
             kc, kc, sl)
+
+
+def noalloc(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, scale=0.1,
+            ns=0, lse=None):
+    return attn.lib().attn_decode_noalloc(q, kc, vc, sl, o, B, Hq, Hkv, D,
+                                          scale, ns, lse, None)
+
+
+def test_decode_noalloc_argument_errors():
+    # host checks only: every call below is refused before any HIP call
+    assert noalloc(B=-1) == -2
+    assert noalloc(Hq=8, Hkv=3) == -3
+    assert noalloc(D=80) == -4
+    assert noalloc(ns=-1) == -7
+    assert noalloc(ns=attn.MAX_SPLITS + 1) == -7
+    # a workspace larger than the library's array
+    big = dict(B=4096, Hq=8, Hkv=8, D=128, ns=attn.MAX_SPLITS)
+    assert attn.attn_decode_workspace_size(4096, 8, 8, 128, attn.MAX_SPLITS) \
+        > attn.NOALLOC_SCRATCH_BYTES
+    assert noalloc(**big) == -6
+    assert noalloc(B=0, q=None, kc=None, vc=None, sl=None, o=None) == 0
