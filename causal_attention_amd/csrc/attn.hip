@@ -7,6 +7,8 @@
 #include <atomic>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "decode.hpp"
 #include "kvcache.hpp"
@@ -114,7 +116,38 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-// 16-bit inputs (bf16 or fp16): the MFMA kernel for element type T.
+// Prefill kernel configurations for 16-bit inputs:
+//   rb: 2-wave workgroups, 64 query rows per wave (attn_prefill_rb_kernel;
+//       head dim 128 only);
+//   pp: the 8-wave ping-pong kernel (attn_prefill_pp_kernel);
+//   w4: the 4-wave kernel, two workgroups per compute unit
+//       (attn_prefill_kernel).
+// The table picks one from the shape; the environment variable
+// ATTN_PREFILL_CFG (pp | w4), read once per process, overrides it for
+// tuning sweeps.
+enum class PrefillCfg { kAuto = 0, kPP = 1, kW4 = 2, kRB = 3 };
+
+PrefillCfg prefill_cfg_override() {
+  static const PrefillCfg cfg = [] {
+    const char* e = getenv("ATTN_PREFILL_CFG");
+    if (e == nullptr) return PrefillCfg::kAuto;
+    if (strcmp(e, "pp") == 0) return PrefillCfg::kPP;
+    if (strcmp(e, "w4") == 0) return PrefillCfg::kW4;
+    if (strcmp(e, "rb") == 0) return PrefillCfg::kRB;
+    return PrefillCfg::kAuto;
+  }();
+  return cfg;
+}
+
+PrefillCfg prefill_cfg(int B, int Hq, int S, int D, int causal) {
+  PrefillCfg o = prefill_cfg_override();
+  if (o == PrefillCfg::kRB && D != 128) o = PrefillCfg::kW4;
+  if (o != PrefillCfg::kAuto) return o;
+  (void)B; (void)Hq; (void)S; (void)causal;
+  return D == 128 ? PrefillCfg::kRB : PrefillCfg::kW4;
+}
+
+// 16-bit inputs (bf16 or fp16): the MFMA kernels for element type T.
 template <typename T>
 struct Half16Prefill {
   template <int D, bool C>
@@ -124,9 +157,27 @@ struct Half16Prefill {
                     int S, float sl2, int nq, int ncu, int use_rope,
                     const attn::RopeRates& rope, const int* cu_seqlens,
                     const int* seq_lens) {
-      hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st,
-                         q, k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu,
-                         use_rope, rope, cu_seqlens, seq_lens);
+      (void)b;
+      const PrefillCfg cfg = prefill_cfg(B, Hq, S, D, C);
+      if constexpr (D == 128) {
+        if (cfg == PrefillCfg::kRB) {
+          hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C>), g,
+                             dim3(attn::kRBThreads), 0, st, q, k, v, o, lse,
+                             B, Hq, Hkv, S, sl2, nq, ncu, use_rope, rope,
+                             cu_seqlens, seq_lens);
+          return;
+        }
+      }
+      if (cfg == PrefillCfg::kW4)
+        hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g,
+                           dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B,
+                           Hq, Hkv, S, sl2, nq, ncu, use_rope, rope,
+                           cu_seqlens, seq_lens);
+      else
+        hipLaunchKernelGGL((attn::attn_prefill_pp_kernel<T, D, C>), g,
+                           dim3(attn::kPPThreads), 0, st, q, k, v, o, lse, B,
+                           Hq, Hkv, S, sl2, nq, use_rope, rope, cu_seqlens,
+                           seq_lens);
     }
   };
 };

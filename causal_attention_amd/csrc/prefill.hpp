@@ -31,6 +31,15 @@ namespace attn {
 
 constexpr int kPrefillThreads = 256;   // 4 waves
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 constexpr int kPrefillBM = 128;        // query rows per workgroup
 
 // Block index -> (batch, KV head, query head, query tile).
@@ -141,6 +150,43 @@ __device__ __forceinline__ void apply_mask_block(f32x16& x, int j0, int hh,
   }
 }
 
+// The same mask as one per-lane limit compared with immediates: key
+// j0 + 8(e/4) + 4 hh + e%4 is dead when it exceeds the last visible key
+// (the query row when causal, S - 1 always).  Computing the limit per tile
+// keeps the compiler from hoisting sixteen comparisons out of a loop.
+// Each element takes -inf through a bit select on the sign of
+// lim - offset, so no lane-mask (SGPR) comparisons are kept alive.
+template <bool CAUSAL>
+__device__ __forceinline__ void apply_mask_lim(f32x16& x, int j0, int hh,
+                                               int query, int S) {
+  const int last = CAUSAL ? min(query, S - 1) : S - 1;
+  const int lim = last - j0 - 4 * hh;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const unsigned dead = (unsigned)((lim - (8 * (e >> 2) + (e & 3))) >> 31);
+    // (through a scalar: a bit cast of the vector element itself reads
+    // element 0 with this compiler)
+    const float xe = x[e];
+    const unsigned bits = __builtin_bit_cast(unsigned, xe);
+    x[e] = __builtin_bit_cast(float, (bits & ~dead) | (0xff800000u & dead));
+  }
+}
+
+// apply_mask_lim on elements e0 .. e0+3 only.
+template <bool CAUSAL>
+__device__ __forceinline__ void apply_mask_lim4(f32x16& x, int e0, int j0,
+                                                int hh, int query, int S) {
+  const int last = CAUSAL ? min(query, S - 1) : S - 1;
+  const int lim = last - j0 - 4 * hh;
+#pragma unroll
+  for (int e = e0; e < e0 + 4; ++e) {
+    const unsigned dead = (unsigned)((lim - (8 * (e >> 2) + (e & 3))) >> 31);
+    const float xe = x[e];
+    const unsigned bits = __builtin_bit_cast(unsigned, xe);
+    x[e] = __builtin_bit_cast(float, (bits & ~dead) | (0xff800000u & dead));
+  }
+}
+
 // ------------------------------------------------- bf16 / fp16 path
 //
 // K and V tiles go global -> LDS with gfx950's direct loads
@@ -228,6 +274,20 @@ __device__ __forceinline__ void lds_buffer_load16(const u32x4& rsrc,
                "buffer_load_dwordx4 %0, %1, %3 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(m),
                   "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+// Load i of a wave's run (see lds_buffer_load16_run) on its own: M0 = l,
+// immediate offset i*1024 on both addresses.
+template <int I>
+__device__ __forceinline__ void lds_buffer_load16_at(const u32x4& rsrc,
+                                                     unsigned voff,
+                                                     unsigned soff, void* l) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds_addr(l));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %0, %2, %3 offen offset:%4 lds"
+               :: "v"(voff), "s"(m), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(I * 1024)
                : "memory", "m0");
 }
 
@@ -503,6 +563,1034 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
           (m_i + fast_log2(l_tot)) * kLn2;
   } else if (seq_lens != nullptr && query < S_all) {
     pad_row(query);
+  }
+}
+
+// ------------------------------------------ 8-wave ping-pong prefill kernel
+//
+// One workgroup of 8 waves per (batch, query head, 128-row query tile).  The
+// waves form two groups of four; both groups hold the same 128 query rows
+// (wave w % 4 owns rows 32 (w % 4) .. +31) and split the key tiles: group g
+// takes tiles g, g + 2, g + 4, ... (32 keys per tile at D = 128, 64 at
+// D = 64, so that each product below is 8 MFMAs).  Each group keeps its own
+// online-softmax state (the merge of key chunks of section 4.4 of the
+// attention-fusion page, done at the end through LDS).
+//
+// Waves w and w + 4 share a SIMD.  Every wave alternates compute phases
+// (8 MFMAs on operands already in registers, interleaved with softmax VALU
+// work) and load phases (LDS -> register reads of the next operand tile,
+// direct global -> LDS loads of a later tile, masking, rescaling), and the
+// two groups run one phase apart, separated by workgroup barriers: while one
+// wave of a SIMD keeps the matrix pipe busy, its partner feeds LDS and
+// memory.  Per group and key tile i (S(i) = raw scores of tile i):
+//   C0(i): S(i+1) = K(i+1) Q^T           || P(i) = exp2(x(i)), l += sum P(i)
+//   L0(i): V(i) LDS -> registers; K(i+NB) global -> LDS; mask S(i+1)
+//   C1(i): O^T += V(i)^T P(i)^T           || row max of S(i+1), reference
+//                                            max, x(i+1) = S(i+1) c - m
+//   L1(i): lazy rescale of O and l; K(i+2) LDS -> registers;
+//          V(i+NB) global -> LDS
+// The scores are double-buffered so that each compute phase has
+// independent VALU work.  K and V tiles of each group sit in a ring of NB
+// LDS slots; a slot is refilled only after every wave of its group has read
+// it, and each wave waits for its own loads of a tile before the barrier
+// that precedes the tile's first read.
+constexpr int kPPThreads = 512;
+constexpr int kPPRing = 4;                   // LDS slots per group
+
+// Block index -> (batch, KV head, query head, query tile): query tiles
+// heaviest first, consecutive blocks walking (batch, KV head) pairs first so
+// that the blocks of one pair share an XCD when the pair count divides 8.
+__device__ __forceinline__ TileCoord tile_coord_lpt(int bid, int Hq, int Hkv,
+                                                    int B, int n_qtiles) {
+  const int G = Hq / Hkv;
+  const int P = B * Hkv;
+  const int pair = bid % P;
+  const int rest = bid / P;
+  TileCoord c;
+  c.b = pair / Hkv;
+  c.g = pair % Hkv;
+  c.hq = c.g * G + rest % G;
+  c.qt = n_qtiles - 1 - rest / G;
+  return c;
+}
+
+// Keep a value computed before this point: the compiler otherwise sinks
+// pure arithmetic past a barrier to the phase that uses it.
+template <typename V>
+__device__ __forceinline__ void pin(V& v) {
+  asm volatile("" : "+v"(v));
+}
+
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads, 1) void attn_prefill_pp_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K,
+    const T* __restrict__ V, T* __restrict__ O,
+    float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
+    float scale_log2, int n_qtiles, int use_rope, RopeRates rope,
+    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
+  constexpr int BM = kPrefillBM;
+  constexpr int TK = D == 128 ? 32 : 64;      // keys per tile
+  constexpr int NSB = TK / 32;                // 32-key sub-blocks per tile
+  constexpr int KT = D / 16;                  // QK k-steps over D
+  constexpr int NDB = D / 32;                 // PV output blocks of 32 dims
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per 1 KB load
+  constexpr int TILE = TK * D * 2;            // bytes per K (or V) tile
+  constexpr int IPW = TILE / 1024 / 4;        // 1 KB loads per wave and tile
+  constexpr int NB = kPPRing;
+  constexpr int SLOT = 2 * TILE;              // K | V
+  constexpr int GROUP = NB * SLOT;            // one group's ring
+  static_assert(TILE == 8192 && IPW == 2, "8 KB tiles, 2 loads per wave");
+  static_assert(NSB * KT == 8 && NSB * 2 * NDB == 8, "8 MFMAs per phase");
+  using E = Elem16<T>;
+  typedef typename E::x8 x8;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * GROUP];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = w >> 2, wq = w & 3;
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const TileCoord tc = tile_coord_lpt(blockIdx.x, Hq, Hkv, B, n_qtiles);
+
+  int S = S_all;
+  size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
+  size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
+  if (cu_seqlens != nullptr) {
+    const int c0 = cu_seqlens[tc.b];
+    S = cu_seqlens[tc.b + 1] - c0;
+    if (tc.qt * BM >= S) return;           // query tile past this sequence
+    q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
+    kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
+  } else if (seq_lens != nullptr) {
+    S = min(max(seq_lens[tc.b], 0), S_all);
+  }
+  // Padding rows [S, S_all): o = 0, lse = -inf.  Group g writes the dims
+  // [g D/2, g D/2 + D/2) of a row (two 16-byte chunks per lane half).
+  auto pad_half_row = [&](int row) {
+    T* orow = O + (q_row0 + row) * D + g * (D / 2) + hh * (D / 4);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{};
+    if (LSE != nullptr && g == 0 && hh == 0) LSE[q_row0 + row] = -INFINITY;
+  };
+  const int q_lo = tc.qt * BM;
+  const int query = q_lo + 32 * wq + r;
+  if (seq_lens != nullptr && q_lo >= S) {
+    if (query < S_all) pad_half_row(query);
+    return;                                 // whole tile is padding
+  }
+  const T* Qp = Q + q_row0 * D;
+  const int q_hi = min(S, q_lo + BM);
+  const int kv_end = CAUSAL ? q_hi : S;
+  const int n_kv = (kv_end + TK - 1) / TK;
+  // Both groups run n = ceil(n_kv / 2) tiles: when n_kv is odd, group 1's
+  // last tile (index n_kv) is a dummy whose keys all lie past the range, so
+  // the mask gives it p = 0 (its loads read valid rows from the start of the
+  // sequence instead).
+  const int n = (n_kv + 1) / 2;
+  // Tiles below n_full need no mask for any row of the workgroup.
+  const int n_full = min(min(n_kv, S / TK), CAUSAL ? (q_lo + 1) / TK : n_kv);
+
+  // Q^T as the MFMA B operand: lane holds query `query`, dims 16t+8hh..+7.
+  x8 qB[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    if (query < S)
+      qB[t] = *reinterpret_cast<const x8*>(Qp + (size_t)query * D +
+                                               16 * t + 8 * hh);
+    else
+      qB[t] = x8{};
+  }
+  if (use_rope) {
+#pragma unroll
+    for (int t = 0; t < KT / 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x1 = (float)qB[t][e], x2 = (float)qB[t + KT / 2][e];
+        const double rr = hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
+        rope_pair(x1, x2, query, rr);
+        qB[t][e] = (T)x1;
+        qB[t + KT / 2][e] = (T)x2;
+      }
+  }
+
+  // Direct loads: wave wq of the group fills 1 KB blocks 2 wq, 2 wq + 1 of
+  // a tile; lane i of block b takes row b RPI + i / CPR, chunk position
+  // i % CPR, i.e. logical chunk swz(row, i % CPR).
+  // voff[ii] = byte offset of the lane's chunk in the tile minus ii KB (the
+  // immediate offset of load ii adds it back).
+  unsigned koffr[IPW], voffr[IPW];
+#pragma unroll
+  for (int ii = 0; ii < IPW; ++ii) {
+    const int row = (wq * IPW + ii) * RPI + lane / CPR, pos = lane % CPR;
+    koffr[ii] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2 - ii * 1024;
+    voffr[ii] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2 - ii * 1024;
+  }
+  const u32x4 krs = buffer_rsrc(K + kv_row0 * D);
+  const u32x4 vrs = buffer_rsrc(V + kv_row0 * D);
+  unsigned char* const gbase = smem + g * GROUP;
+  // K (kv = 0) or V (kv = 1) of this group's tile i into its ring slot.
+  auto issue = [&](int kv, int i) {
+    const int jt = 2 * i + g;
+    const int j0 = jt < n_kv ? jt * TK : 0;    // the dummy tile reads rows 0..
+    const unsigned soff = (unsigned)j0 * D * 2;
+    unsigned char* dst = gbase + (i % NB) * SLOT + kv * TILE +
+                         wq * IPW * 1024;
+    const u32x4& rs = kv ? vrs : krs;
+    if (j0 + TK <= S) {
+      lds_buffer_load16_run<IPW>(rs, kv ? voffr : koffr, soff, dst);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < IPW; ++ii) {
+        const int row = (wq * IPW + ii) * RPI + lane / CPR;
+        const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
+        lds_buffer_load16(rs, (kv ? voffr[ii] : koffr[ii]) + ii * 1024 + back,
+                          soff, dst + ii * 1024);
+      }
+    }
+  };
+
+  // LDS operand reads.  They are plain (compiler-visible) LDS loads: the
+  // barriers are assembly statements with a memory clobber, so no read
+  // moves out of its load phase, and the compiler inserts the LDS waits
+  // before the first use.  (The direct global -> LDS loads are assembly the
+  // compiler does not see, so it never waits on them.)  Per-lane offsets
+  // from the group's ring; slot and row steps fold into the instruction's
+  // immediate offset (the swizzles repeat every 8 rows).
+  const int grp = lane >> 4, jl = lane & 15;
+  const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
+  const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
+  x8 kreg[NSB * KT];                 // K operands of the next QK
+  x8 vop[NSB * 2 * NDB];             // V operands of the next PV
+  auto read_k = [&](auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const int row = sb * 32 + r;
+        kreg[sb * KT + t] = *reinterpret_cast<const x8*>(
+            gbase + SL * SLOT + (row * D + 8 * swz_k<CPR>(row, 2 * t + hh)) * 2);
+      }
+  };
+  auto read_v = [&](auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const T* Vt = reinterpret_cast<const T*>(gbase + SL * SLOT + TILE);
+#pragma unroll
+    for (int su = 0; su < NSB * 2; ++su)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row0 = su * 16 + vrow_off;
+        const int col = db * 32 + vcol_off;
+        const int c = col >> 3, e = col & 7;
+        const u32x2 lo = lds_read_tr16(Vt + row0 * D +
+                                       8 * swz_v<CPR>(row0, c) + e);
+        const u32x2 hi = lds_read_tr16(Vt + (row0 + 8) * D +
+                                       8 * swz_v<CPR>(row0 + 8, c) + e);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        vop[su * NDB + db] = __builtin_bit_cast(x8, a);
+      }
+  };
+
+  // Online-softmax state (per lane: one query row, half of each tile's
+  // keys): reference max m_ref (log2 domain, scale folded in), lane-partial
+  // sum l_i, O^T accumulators, pending rescale factor.
+  f32x16 oacc[NDB];                 // zeroed after the prologue
+  float m_ref = -INFINITY, l_i = 0.f, alpha = 1.f;
+  bool pend = false;
+  f32x16 sbuf[2][NSB];
+  x8 pP[NSB][2];
+
+  auto qk = [&](auto buf_c) {
+    constexpr int SB = decltype(buf_c)::value;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      sbuf[SB][sb] = E::mma32(kreg[sb * KT], qB[0], f32x16{});
+#pragma unroll
+      for (int t = 1; t < KT; ++t)
+        sbuf[SB][sb] = E::mma32(kreg[sb * KT + t], qB[t], sbuf[SB][sb]);
+    }
+  };
+  auto pv = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          oacc[db] = E::mma32(vop[(sb * 2 + uu) * NDB + db], pP[sb][uu],
+                              oacc[db]);
+        }
+  };
+  // Causal / tail mask of the raw scores of tile i (group-local index).
+  auto mask = [&](auto buf_c, int i) {
+    constexpr int SB = decltype(buf_c)::value;
+    const int j0 = (2 * i + g) * TK;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+      apply_mask_block<CAUSAL>(sbuf[SB][sb], j0 + 32 * sb, hh, query, S);
+  };
+  // Row max of tile scores, new reference when it grows by more than 2^8
+  // (valid tiles only), then x = s c - m_ref in place.
+  auto alu0 = [&](auto buf_c, bool valid) {
+    constexpr int SB = decltype(buf_c)::value;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const f32x16& sv = sbuf[SB][sb];
+      float t0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+      float t1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+      float t2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
+      float t3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+      float t4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
+      mx = fmaxf(fmaxf(mx, fmaxf(fmaxf(t0, t1), t2)),
+                 fmaxf(fmaxf(t3, t4), sv[15]));
+    }
+    mx = max_halves(mx) * scale_log2;
+    const bool up = valid && (mx > m_ref + kLazyRescale);
+    const float m_new = up ? mx : m_ref;
+    alpha = up ? fast_exp2(m_ref - m_new) : alpha;
+    pend = pend || up;
+    m_ref = m_new;
+    // a row with no visible key yet keeps m_ref = -inf and gets p = 0
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sbuf[SB][sb][e] = fmaf(sbuf[SB][sb][e], scale_log2, neg_m);
+  };
+  auto alu1 = [&](auto buf_c) {
+    constexpr int SB = decltype(buf_c)::value;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(sbuf[SB][sb][8 * uu + e]);
+          if (e & 1) s1 += p; else s0 += p;
+          pP[sb][uu][e] = (T)p;
+        }
+    l_i += s0 + s1;
+  };
+  auto rescale = [&]() {
+    if (__ballot(pend)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      l_i *= alpha;
+      alpha = 1.f;
+      pend = false;
+    }
+  };
+  // Interleave MFMAs with the phase's softmax work.
+  auto sched_c0 = [&]() {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+  auto sched_c1 = [&]() {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+  };
+
+  // ---- prologue: Q (above), the first NB tiles, S(0); K(1) and V(0) in
+  // registers.  n >= 1: every query tile has a visible key.
+  for (int i = 0; i < NB && i < n; ++i) {
+    issue(0, i);
+    issue(1, i);
+  }
+  if (n >= NB) wait_vmem_le<(2 * NB - 1) * IPW>(); else wait_vmem();
+  wg_barrier();
+  read_k(std::integral_constant<int, 0>{});
+  qk(std::integral_constant<int, 0>{});
+  if (g >= n_full) mask(std::integral_constant<int, 0>{}, 0);
+  alu0(std::integral_constant<int, 0>{}, true);
+  alpha = 1.f;
+  pend = false;                      // O and l are zero: nothing to rescale
+  if (n >= NB) wait_vmem_le<(2 * NB - 3) * IPW>(); else wait_vmem();
+  wg_barrier();
+  read_k(std::integral_constant<int, 1>{});   // stale data when n == 1
+  read_v(std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+
+  // ---- main loop.  Per tile i of the group (U = i % NB) a compute phase C
+  // and a load phase L; group 1 runs one phase behind group 0, so on every
+  // SIMD one wave computes while the other loads.
+  //   C(i): S(i+1) = K(i+1) Q^T || P(i) = exp2(x(i)), l += sum P(i);
+  //         [mask S(i+1)];  O^T += V(i)^T P(i)^T || row max of S(i+1),
+  //         reference, x(i+1) = S(i+1) c - m
+  //   L(i): lazy rescale; K(i+2), V(i+1) LDS -> registers;
+  //         K(i+NB), V(i+NB) global -> LDS
+  auto C = [&](auto u_c, int i) {
+    constexpr int U = decltype(u_c)::value;
+    using Bc = std::integral_constant<int, U & 1>;
+    using Bn = std::integral_constant<int, (U + 1) & 1>;
+    qk(Bn{});                                   // stale on the last tile
+    alu1(Bc{});
+    sched_c0();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      pin(pP[sb][0]);
+      pin(pP[sb][1]);
+    }
+    pin(l_i);
+    if (i + 1 < n && 2 * (i + 1) + g >= n_full) mask(Bn{}, i + 1);
+    pv();
+    alu0(Bn{}, i + 1 < n);
+    sched_c1();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) pin(sbuf[(U + 1) & 1][sb]);
+    pin(m_ref);
+    pin(alpha);
+    // K(i+2) (and the older V(i+1)) must have landed before L(i)
+    if (i + NB - 1 < n) wait_vmem_le<(2 * NB - 5) * IPW>(); else wait_vmem();
+  };
+  auto L = [&](auto u_c, int i) {
+    constexpr int U = decltype(u_c)::value;
+    rescale();
+    read_k(std::integral_constant<int, (U + 2) % NB>{});  // stale at the end
+    read_v(std::integral_constant<int, (U + 1) % NB>{});
+    if (i + NB < n) {
+      issue(0, i + NB);
+      issue(1, i + NB);
+    }
+  };
+  // Each group runs its own copy of the loop (same number of barriers).
+  auto step = [&](auto g_c, auto u_c, int it) {
+    constexpr int GG = decltype(g_c)::value;
+    constexpr int U = decltype(u_c)::value;
+    using Uc = std::integral_constant<int, U>;
+    using Up = std::integral_constant<int, (U + NB - 1) % NB>;
+    if constexpr (GG == 0) {
+      C(Uc{}, it);
+      wg_barrier();
+      L(Uc{}, it);
+      wg_barrier();
+    } else {
+      if (it > 0) L(Up{}, it - 1);
+      wg_barrier();
+      C(Uc{}, it);
+      wg_barrier();
+    }
+  };
+  static_assert(NB == 4, "the loop is unrolled by the ring size");
+  auto run_loop = [&](auto g_c) {
+    for (int it = 0; it < n; it += 4) {
+      step(g_c, std::integral_constant<int, 0>{}, it);
+      if (it + 1 < n) step(g_c, std::integral_constant<int, 1>{}, it + 1);
+      if (it + 2 < n) step(g_c, std::integral_constant<int, 2>{}, it + 2);
+      if (it + 3 < n) step(g_c, std::integral_constant<int, 3>{}, it + 3);
+    }
+  };
+  if (g == 0)
+    run_loop(std::integral_constant<int, 0>{});
+  else
+    run_loop(std::integral_constant<int, 1>{});
+  // group 1's last L is a no-op (no tile after its last), and every load
+  // has been consumed: the ring is free for the merge.
+  wait_vmem();
+  rescale();
+
+  // ---- merge the two groups' states and write O, LSE.  Group g finishes
+  // dims [g D/2, g D/2 + D/2) of its rows: it sends the other half of its
+  // accumulators (and m_ref, l) through LDS and merges what it receives.
+  constexpr int NDH = NDB / 2;
+  const float l_tot = l_i + swap_halves(l_i);
+  float2* xm = reinterpret_cast<float2*>(smem + 64 * 1024);
+  // The accumulator index must be a compile-time constant (a runtime index
+  // would move the whole array to scratch memory), so each group has its
+  // own instance of the exchange.
+  auto merge = [&](auto g_c) {
+    constexpr int GG = decltype(g_c)::value;
+    f32x4* xo = reinterpret_cast<f32x4*>(smem + GG * (32 * 1024));
+    const f32x4* xi =
+        reinterpret_cast<const f32x4*>(smem + (GG ^ 1) * (32 * 1024));
+#pragma unroll
+    for (int d = 0; d < NDH; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int db = (GG ^ 1) * NDH + d;       // the other group's half
+        xo[((wq * NDH + d) * 4 + a) * 64 + lane] =
+            f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
+                  oacc[db][4 * a + 3]};
+      }
+    xm[(GG * 4 + wq) * 64 + lane] = make_float2(m_ref, l_tot);
+    __syncthreads();
+    const float2 mo = xm[((GG ^ 1) * 4 + wq) * 64 + lane];
+    const float m = fmaxf(m_ref, mo.x);
+    const float a_own = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m);
+    const float a_oth = (mo.x == -INFINITY) ? 0.f : fast_exp2(mo.x - m);
+    const float L = l_tot * a_own + mo.y * a_oth;
+    if (query < S) {
+      const float inv = 1.f / L;
+      T* orow = O + (q_row0 + query) * D;
+#pragma unroll
+      for (int d = 0; d < NDH; ++d) {
+        const int db = GG * NDH + d;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 other = xi[((wq * NDH + d) * 4 + a) * 64 + lane];
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (oacc[db][4 * a + e] * a_own + other[e] * a_oth) * inv;
+          u32x2 pr;
+          pr[0] = E::pack2(v[0], v[1]);
+          pr[1] = E::pack2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hh) = pr;
+        }
+      }
+      if (LSE != nullptr && GG == 0 && hh == 0)
+        LSE[q_row0 + query] = (m + fast_log2(L)) * kLn2;
+    } else if (seq_lens != nullptr && query < S_all) {
+      pad_half_row(query);
+    }
+  };
+  if (g == 0)
+    merge(std::integral_constant<int, 0>{});
+  else
+    merge(std::integral_constant<int, 1>{});
+}
+
+// ------------------------------------- register-blocked prefill kernel
+//
+// One workgroup of 2 waves per (batch, query head, 128-row query tile), two
+// workgroups per compute unit: one wave per SIMD.  Each wave owns 64 query
+// rows as two 32-row blocks, so every K or V operand read from LDS feeds two
+// MFMAs (half the LDS traffic per MFMA of a 32-row wave).  With 512
+// registers per wave, Q and the output accumulators live in the
+// accumulation registers (AGPRs), which only MFMAs read; scores,
+// probabilities and the K / V operands are VGPRs.  The QK^T products are
+// issued as inline assembly so that the scores land in VGPRs (the compiler
+// otherwise puts every MFMA result in AGPRs and copies the scores back).
+//
+// Fixed reference.  Each row keeps the max of its first key tile (every row
+// sees key 0) as the reference m of the online softmax of section 2.2 of the
+// attention-fusion page, and never rescales: later probabilities
+// p = 2^(x - m) may exceed 1, and O / l and LSE = m + log2 l are exact for
+// any reference.  While every score stays below m + h, p < 2^h: h = 15 for
+// fp16 probabilities (largest finite value 65504), 32 for bf16 (fp32 sums
+// of p v then overflow only for |v| beyond 2^70); a row whose score goes
+// higher makes the workgroup redo its tile with m set to that row's true
+// max (tracked during the first pass), so that p <= 1 in the second pass.
+// Without a rescale no VALU ever touches the accumulators inside the loop.
+//
+// With no second wave on the SIMD, each wave overlaps its own softmax with
+// its MFMAs through a software pipeline across 32-key tiles (scores
+// double-buffered); per tile i:
+//   A(i): V(i) LDS -> registers; S(i+1) = K(i+1) Q^T  interleaved with
+//         P(i) = exp2(x(i)), l += sum P(i)
+//   B(i): O^T += V(i)^T P(i)^T  interleaved with the row max of S(i+1) and
+//         x(i+1) = S(i+1) c - m; K(i+2) LDS -> registers
+// then a wait for this wave's loads of the next tiles, one barrier (both
+// waves' loads visible, both waves' reads of tile i done) and the direct
+// global -> LDS loads of tile i + NB into tile i's slot.
+//
+// The QK^T products being assembly, the wait states the hardware needs
+// between their results and a VALU read are inserted here (s_nop), with
+// margin over what the compiler emits for the same dependency.
+constexpr int kRBThreads = 128;
+constexpr int kRBRing = 4;
+constexpr int kRBMaxPasses = 8;
+// log2 headroom over the reference for probabilities of type T
+template <typename T>
+constexpr float rb_headroom() {
+  return std::is_same<T, _Float16>::value ? 15.f : 32.f;
+}
+
+template <typename T>
+struct MfmaAsm;
+template <>
+struct MfmaAsm<__bf16> {
+  // d (VGPR) = a (VGPR) b (AGPR), and d += a b
+  static __device__ __forceinline__ void qk0(f32x16& d, const u32x4& a,
+                                             const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                 : "=&v"(d) : "v"(a), "a"(b));
+  }
+  static __device__ __forceinline__ void qk(f32x16& d, const u32x4& a,
+                                            const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+v"(d) : "v"(a), "a"(b));
+  }
+};
+template <>
+struct MfmaAsm<_Float16> {
+  static __device__ __forceinline__ void qk0(f32x16& d, const u32x4& a,
+                                             const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
+                 : "=&v"(d) : "v"(a), "a"(b));
+  }
+  static __device__ __forceinline__ void qk(f32x16& d, const u32x4& a,
+                                            const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                 : "+v"(d) : "v"(a), "a"(b));
+  }
+};
+
+// Wait states after an MFMA result before a VALU reads it (19).  The two
+// score blocks the assembly MFMAs wrote pass through the statement: every
+// read of them then depends on it (none is scheduled above the wait), and
+// their registers hold them until it, so no other value is placed there
+// while the MFMAs, unseen by the compiler, still write back.
+__device__ __forceinline__ void mfma_to_valu_wait(f32x16& s0, f32x16& s1) {
+  asm volatile("s_nop 15\n\ts_nop 2" : "+v"(s0), "+v"(s1));
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K,
+    const T* __restrict__ V, T* __restrict__ O,
+    float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
+    float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
+    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
+  static_assert(D == 128, "64 rows per wave at head dim 128");
+  constexpr int BM = kPrefillBM;              // 128 rows per workgroup
+  constexpr int TK = 32;                      // keys per tile
+  constexpr int KT = D / 16;                  // QK k-steps
+  constexpr int NDB = D / 32;                 // PV output blocks
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per 1 KB load
+  constexpr int TILE = TK * D * 2;            // 8 KB per K (or V) tile
+  constexpr int IPW = TILE / 1024 / 2;        // 4 loads per wave and tile
+  constexpr int NB = kRBRing;
+  constexpr int SLOT = 2 * TILE;
+  using E = Elem16<T>;
+  using M = MfmaAsm<T>;
+  typedef typename E::x8 x8;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NB * SLOT];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const TileCoord tc =
+      tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
+
+  int S = S_all;
+  size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
+  size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
+  if (cu_seqlens != nullptr) {
+    const int c0 = cu_seqlens[tc.b];
+    S = cu_seqlens[tc.b + 1] - c0;
+    if (tc.qt * BM >= S) return;
+    q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
+    kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
+  } else if (seq_lens != nullptr) {
+    S = min(max(seq_lens[tc.b], 0), S_all);
+  }
+  // o = 0, lse = -inf for a padding row (one half row per lane half).
+  auto pad_row = [&](int row) {
+    T* orow = O + (q_row0 + row) * D + hh * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{};
+    if (LSE != nullptr && hh == 0) LSE[q_row0 + row] = -INFINITY;
+  };
+  const int q_lo = tc.qt * BM;
+  const int wq0 = q_lo + 64 * w;              // first row of this wave
+  if (seq_lens != nullptr && q_lo >= S) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      if (wq0 + 32 * rb + r < S_all) pad_row(wq0 + 32 * rb + r);
+    return;
+  }
+  const T* Qp = Q + q_row0 * D;
+  const int q_hi = min(S, q_lo + BM);
+  const int kv_end = CAUSAL ? q_hi : S;
+  const int n = (kv_end + TK - 1) / TK;       // key tiles (>= 1)
+  const int n_full = min(min(n, S / TK), CAUSAL ? (q_lo + 1) / TK : n);
+
+  // Q^T B operands of both row blocks (AGPRs, through the QK^T assembly).
+  u32x4 qB[2][KT];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int query = wq0 + 32 * rb + r;
+    x8 qv[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      qv[t] = query < S ? *reinterpret_cast<const x8*>(
+                              Qp + (size_t)query * D + 16 * t + 8 * hh)
+                        : x8{};
+    if (use_rope) {
+#pragma unroll
+      for (int t = 0; t < KT / 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float x1 = (float)qv[t][e], x2 = (float)qv[t + KT / 2][e];
+          const double rr = hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
+          rope_pair(x1, x2, query, rr);
+          qv[t][e] = (T)x1;
+          qv[t + KT / 2][e] = (T)x2;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qB[rb][t] = __builtin_bit_cast(u32x4, qv[t]);
+  }
+
+  // Direct loads: wave w fills 1 KB blocks 4w .. 4w+3 of a tile.
+  unsigned koffr[IPW], voffr[IPW];
+#pragma unroll
+  for (int ii = 0; ii < IPW; ++ii) {
+    const int row = (w * IPW + ii) * RPI + lane / CPR, pos = lane % CPR;
+    koffr[ii] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2 - ii * 1024;
+    voffr[ii] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2 - ii * 1024;
+  }
+  const u32x4 krs = buffer_rsrc(K + kv_row0 * D);
+  const u32x4 vrs = buffer_rsrc(V + kv_row0 * D);
+  // Load II of this wave's share of K (kv = 0) or V (kv = 1) tile j into
+  // ring slot j % NB.  A tile past the last one holding keys loads that one
+  // instead (its slot is not read again); rows past S load row S - 1 (their
+  // scores are masked).
+  const int jmax = (S - 1) / TK;
+  auto issue1 = [&](int kv, int j, auto ii_c, auto full_c) {
+    constexpr int II = decltype(ii_c)::value;
+    if constexpr (decltype(full_c)::value) {   // tile j known full
+      unsigned char* dst = smem + (j % NB) * SLOT + kv * TILE + w * IPW * 1024;
+      lds_buffer_load16_at<II>(kv ? vrs : krs, kv ? voffr[II] : koffr[II],
+                               (unsigned)j * (TK * D * 2), dst);
+      return;
+    }
+    const int j0 = min(j, jmax) * TK;
+    const unsigned soff = (unsigned)j0 * D * 2;
+    unsigned char* dst = smem + (j % NB) * SLOT + kv * TILE + w * IPW * 1024;
+    const u32x4& rs = kv ? vrs : krs;
+    const unsigned voff = kv ? voffr[II] : koffr[II];
+    if (j0 + TK <= S) {
+      lds_buffer_load16_at<II>(rs, voff, soff, dst);
+    } else {
+      const int row = (w * IPW + II) * RPI + lane / CPR;
+      const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
+      lds_buffer_load16(rs, voff + II * 1024 + back, soff, dst + II * 1024);
+    }
+  };
+  auto issue = [&](int kv, int j) {
+    static_for<IPW>([&](auto ii) { issue1(kv, j, ii, std::false_type{}); });
+  };
+
+  u32x4 kreg[KT];                      // K operands of the next QK
+  u32x4 vop[2 * NDB];                  // V operands of the next PV
+  const int grp = lane >> 4, jl = lane & 15;
+  const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
+  const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
+  auto read_k1 = [&](auto slot_c, int t) {
+    constexpr int SL = decltype(slot_c)::value;
+    kreg[t] = *reinterpret_cast<const u32x4*>(
+        smem + SL * SLOT + (r * D + 8 * swz_k<CPR>(r, 2 * t + hh)) * 2);
+  };
+  auto read_v = [&](auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const T* Vt = reinterpret_cast<const T*>(smem + SL * SLOT + TILE);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row0 = u * 16 + vrow_off;
+        const int col = db * 32 + vcol_off;
+        const int c = col >> 3, e = col & 7;
+        const u32x2 lo = lds_read_tr16(Vt + row0 * D +
+                                       8 * swz_v<CPR>(row0, c) + e);
+        const u32x2 hi = lds_read_tr16(Vt + (row0 + 8) * D +
+                                       8 * swz_v<CPR>(row0 + 8, c) + e);
+        vop[u * NDB + db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+  };
+
+  f32x16 oacc[2][NDB];
+  float m_ref[2], l_i[2];
+  f32x16 sbuf[2][2];                   // [buffer][row block]
+  u32x4 pP[2][2];                      // [row block][k-step], packed pairs
+
+  // QK^T slot s of a tile: k-step s/2 of row block s%2 (consecutive slots
+  // are independent MFMAs; a row block's chain advances every other slot).
+  auto qk_slot = [&](auto buf_c, int s) {
+    constexpr int SB = decltype(buf_c)::value;
+    const int t = s >> 1, rb = s & 1;
+    if (t == 0) M::qk0(sbuf[SB][rb], kreg[0], qB[rb][0]);
+    else M::qk(sbuf[SB][rb], kreg[t], qB[rb][t]);
+  };
+  // Causal / tail mask of elements e0 .. e0+3 of row block rb of buffer SB
+  // for key tile i.
+  auto mask4 = [&](auto buf_c, int rb, int e0, int i) {
+    constexpr int SB = decltype(buf_c)::value;
+    apply_mask_lim4<CAUSAL>(sbuf[SB][rb], e0, i * TK, hh, wq0 + 32 * rb + r,
+                            S);
+  };
+  // Row max (log2 domain) of one row block of buffer SB.
+  auto rowmax = [&](auto buf_c, int rb) {
+    constexpr int SB = decltype(buf_c)::value;
+    const f32x16& sv = sbuf[SB][rb];
+    float t0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+    float t1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+    float t2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
+    float t3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+    float t4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
+    const float mx =
+        fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), sv[15]));
+    return max_halves(mx) * scale_log2;
+  };
+  // x = s c - m for elements e0 .. e0+3 of row block rb.
+  auto fma4 = [&](auto buf_c, int rb, int e0, float neg_m) {
+    constexpr int SB = decltype(buf_c)::value;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sbuf[SB][rb][e0 + e] = fmaf(sbuf[SB][rb][e0 + e], scale_log2, neg_m);
+  };
+  // Pair p of a tile: elements 2(p%8), 2(p%8)+1 of row block p/8.  The
+  // probabilities replace the scores in place (summed into l later).
+  auto exp_pair = [&](auto buf_c, int p, float& e0, float& e1) {
+    constexpr int SB = decltype(buf_c)::value;
+    const int rb = p >> 3, e = 2 * (p & 7);
+    e0 = sbuf[SB][rb][e] = fast_exp2(sbuf[SB][rb][e]);
+    e1 = sbuf[SB][rb][e + 1] = fast_exp2(sbuf[SB][rb][e + 1]);
+  };
+  auto use_pair = [&](int p, float e0, float e1) {
+    const int rb = p >> 3, e = 2 * (p & 7);
+    pP[rb][e >> 3][(e & 7) >> 1] = E::pack2(e0, e1);
+  };
+  // l += pair p of buffer SB (fp32 probabilities).
+  auto sum_pair = [&](auto buf_c, int p) {
+    constexpr int SB = decltype(buf_c)::value;
+    const int rb = p >> 3, e = 2 * (p & 7);
+    l_i[rb] = (l_i[rb] + sbuf[SB][rb][e]) + sbuf[SB][rb][e + 1];
+  };
+
+  // One pass over the key tiles with reference m_ref: each row's first-tile
+  // max in pass 0, the bound computed after the previous pass otherwise.
+  using B0 = std::integral_constant<int, 0>;
+  auto run_pass = [&](int pass, const float (&m_next)[2]) {
+    // ---- prologue: K0 K1 K2 V0 K3 V1 V2 in flight, then S(0), then K4
+    // into K0's slot; K(1) in registers.  From here on tile t loads K(t+5)
+    // and V(t+3) (every load is issued, past the end too, so the counts of
+    // loads in flight are fixed).
+    issue(0, 0);
+    issue(0, 1);
+    issue(0, 2);
+    issue(1, 0);
+    issue(0, 3);
+    issue(1, 1);
+    issue(1, 2);
+    wait_vmem_le<6 * IPW>();                  // K0
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < KT; ++t) read_k1(B0{}, t);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qk_slot(B0{}, s);
+    mfma_to_valu_wait(sbuf[0][0], sbuf[0][1]);
+    if (0 >= n_full) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e0 = 0; e0 < 16; e0 += 4) mask4(B0{}, rb, e0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      m_ref[rb] = pass == 0 ? rowmax(B0{}, rb) : m_next[rb];
+#pragma unroll
+      for (int e0 = 0; e0 < 16; e0 += 4) fma4(B0{}, rb, e0, -m_ref[rb]);
+      l_i[rb] = 0.f;
+    }
+    // the first tile reads K(1) now, V(0) and K(2) next
+    wait_vmem_le<3 * IPW>();                  // K1, K2, V0
+    __syncthreads();
+    issue(0, 4);
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      read_k1(std::integral_constant<int, 1>{}, t);   // stale when n == 1
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[rb][db] = f32x16{};
+
+    // ---- main loop (unrolled by the ring size so slots are immediates).
+    // Each MFMA is followed by at most about one MFMA's duration of VALU
+    // work: a second MFMA issued while the first still runs stalls the
+    // wave, and with it the VALU work queued behind it.  The loads of a
+    // tile are spread over its QK slots: issued back to back, they stall
+    // the wave for several hundred cycles.
+    // FULL: the tiles this one loads (K(i+5), V(i+3)) are full tiles.
+    auto tile = [&](auto u_c, auto masked_c, auto full_c, int i) {
+      constexpr int U = decltype(u_c)::value;
+      constexpr bool MASKED = decltype(masked_c)::value;
+      using Bc = std::integral_constant<int, U & 1>;
+      using Bn = std::integral_constant<int, (U + 1) & 1>;
+      using Sv = std::integral_constant<int, U>;
+      using Sk = std::integral_constant<int, (U + 2) % NB>;
+      // A(i): V(i) reads; 16 QK MFMAs of S(i+1), each followed by the
+      // exponentials of one pair of scores of tile i and the packing of the
+      // previous pair, every other one by a load of K(i+5) or V(i+3).
+      read_v(Sv{});
+      float pe0, pe1;
+      exp_pair(Bc{}, 0, pe0, pe1);
+      static_for<16>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        qk_slot(Bn{}, s);                      // stale on the last tile
+        __builtin_amdgcn_sched_barrier(0);
+        float ne0 = 0.f, ne1 = 0.f;
+        if (s + 1 < 16) exp_pair(Bc{}, s + 1, ne0, ne1);
+        use_pair(s, pe0, pe1);
+        pe0 = ne0;
+        pe1 = ne1;
+        if constexpr ((s & 1) != 0) {
+          constexpr int q = s >> 1;
+          if constexpr (q < IPW)
+            issue1(0, i + 5, std::integral_constant<int, q>{}, full_c);
+          else
+            issue1(1, i + 3, std::integral_constant<int, q - IPW>{}, full_c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        pin(sbuf[U & 1][rb]);
+        pin(pP[rb][0]);
+        pin(pP[rb][1]);
+      }
+      // B(i): 16 PV MFMAs, each followed by a slice of the row sums of P(i),
+      // of the K(i+2) reads, of the mask of S(i+1) (tiles that need one) and
+      // of x(i+1) = S(i+1) c - m.
+      const float nm0 = -m_ref[0], nm1 = -m_ref[1];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int u = k >> 3, db = (k >> 1) & 3, rb = k & 1;
+        oacc[rb][db] = E::mma32(__builtin_bit_cast(x8, vop[u * NDB + db]),
+                                __builtin_bit_cast(x8, pP[rb][u]),
+                                oacc[rb][db]);
+        __builtin_amdgcn_sched_barrier(0);
+        // S(i+1) complete (the wait overlaps this MFMA)
+        if (k == 0) mfma_to_valu_wait(sbuf[(U + 1) & 1][0],
+                                      sbuf[(U + 1) & 1][1]);
+        if (k < KT) read_k1(Sk{}, k);          // stale at the end
+        sum_pair(Bc{}, k);
+        if constexpr (MASKED) {
+          if (k >= 1 && k < 9) {
+            const int j = k - 1;               // 8 slices of 4 elements
+            mask4(Bn{}, j >> 2, 4 * (j & 3), i + 1);
+          }
+          if (k >= 8) {
+            const int j = k - 8;
+            fma4(Bn{}, j >> 2, 4 * (j & 3), (j >> 2) ? nm1 : nm0);
+          }
+        } else {
+          if (k >= 1 && k < 9) {
+            const int j = k - 1;
+            fma4(Bn{}, j >> 2, 4 * (j & 3), (j >> 2) ? nm1 : nm0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        pin(l_i[rb]);
+        pin(sbuf[(U + 1) & 1][rb]);
+      }
+      // Before the barrier: this wave's loads of the tiles read next
+      // (V(i+1), K(i+3), issued two tiles ago; the loads of the last two
+      // tiles may still run) have landed and its LDS reads of tile i are
+      // complete; after it, the slots of V(i) and K(i+2) may be refilled.
+      wait_vmem_le<4 * IPW>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+      wg_barrier();
+    };
+    // Tiles whose successor needs no mask and whose loads are full tiles
+    // run in a loop without mask or tail code; the last few (the diagonal,
+    // a ragged tail, loads past the end) in one that always masks, so that
+    // no branch in either loop rewrites the scores.
+    static_assert(NB == 4, "the loop is unrolled by the ring size");
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    using Plain = std::false_type;
+    using Masked = std::true_type;
+    using Full = std::true_type;
+    using Any = std::false_type;
+    const int n_plain = min(n_full, S / TK - 5);   // it + 8 < S / TK
+    int it = 0;
+    for (; it + 4 < n_plain; it += 4) {
+      tile(C0{}, Plain{}, Full{}, it);
+      tile(C1{}, Plain{}, Full{}, it + 1);
+      tile(C2{}, Plain{}, Full{}, it + 2);
+      tile(C3{}, Plain{}, Full{}, it + 3);
+    }
+    for (; it < n; it += 4) {
+      tile(C0{}, Masked{}, Any{}, it);
+      if (it + 1 < n) tile(C1{}, Masked{}, Any{}, it + 1);
+      if (it + 2 < n) tile(C2{}, Masked{}, Any{}, it + 2);
+      if (it + 3 < n) tile(C3{}, Masked{}, Any{}, it + 3);
+    }
+    wait_vmem();
+  };
+  // Passes.  After a pass, a row whose sum l outgrew 2^h (or overflowed
+  // fp32) had a probability above the headroom: the workgroup runs its tile
+  // again (the two waves agree through LDS; every load has landed and every
+  // LDS read is done at the loop's last barrier) with m = m + log2 l, which
+  // bounds every score of the row from above (l >= each p), so that p <= 1;
+  // after an fp32 overflow (some p >= 2^128 / S), m + 100 is still below the
+  // row's max.  Rows within the headroom take the new m as well.
+  float m_next[2] = {0.f, 0.f};
+  constexpr float kLimit = (float)(1ull << (int)rb_headroom<T>());
+  for (int pass = 0; pass < kRBMaxPasses; ++pass) {
+    run_pass(pass, m_next);
+    bool over = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float l_tot = l_i[rb] + swap_halves(l_i[rb]);
+      const bool inf = l_tot == INFINITY;
+      over = over || inf || l_tot > kLimit;
+      m_next[rb] = m_ref[rb] + (inf ? 100.f : fast_log2(l_tot));
+    }
+    int* flag = reinterpret_cast<int*>(smem);
+    const int any = __ballot(over) != 0;      // with every lane active
+    if (lane == 0) flag[w] = any;
+    __syncthreads();
+    const bool again = (flag[0] | flag[1]) != 0;
+    __syncthreads();
+    if (!again) break;
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m_ref + log2 l) ln 2
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int query = wq0 + 32 * rb + r;
+    const float l_tot = l_i[rb] + swap_halves(l_i[rb]);
+    if (query < S) {
+      const float inv = 1.f / l_tot;
+      T* orow = O + (q_row0 + query) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 pr;
+          pr[0] = E::pack2(oacc[rb][db][4 * a] * inv,
+                           oacc[rb][db][4 * a + 1] * inv);
+          pr[1] = E::pack2(oacc[rb][db][4 * a + 2] * inv,
+                           oacc[rb][db][4 * a + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hh) = pr;
+        }
+      if (LSE != nullptr && hh == 0)
+        LSE[q_row0 + query] = (m_ref[rb] + fast_log2(l_tot)) * kLn2;
+    } else if (seq_lens != nullptr && query < S_all) {
+      pad_row(query);
+    }
   }
 }
 

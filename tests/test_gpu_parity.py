@@ -755,3 +755,35 @@ def test_prefill_varlen_equal_lengths_is_the_dense_kernel():
     torch.cuda.synchronize()
     assert torch.equal(o.view(B, Hq, S, D), do)
     assert torch.equal(lse.view(B, Hq, S), dl)
+
+
+# ------------------------------------------- a late, far larger row maximum
+
+@pytest.mark.parametrize("boost", [8.0, 1.5])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_late_dominant_key(dtype, causal, boost):
+    """One late key aligned with every query row of head 0 and `boost` times
+    as long.  boost 8: its score exceeds each row's first-tile maximum by
+    about 130 log2 units, past any headroom a kernel may keep over a
+    reference maximum; boost 1.5: by about 20, above the headroom of fp16
+    probabilities but not of bf16 ones.  The result must match the oracle,
+    and for boost 8 the rows that see the key take its value."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 1100, 128
+    say(f"[prefill late dominant key] {dtype} causal={causal} boost={boost}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, dtype, 1.0, 12)
+    j = 1000
+    q[:, 0] = q[:, 0, :1]
+    k[:, 0, j] = (q[:, 0, 0].float() * boost).to(q.dtype)
+    o, lse = attn.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(np64(q), np64(k), np64(v), 1 / math.sqrt(D),
+                            causal)
+    eo, el = np.abs(np64(o) - ro).max(), np.abs(lse.cpu().numpy() - rl).max()
+    say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert np.isfinite(np64(o)).all()
+    assert eo <= o_tol(dtype) and el <= LSE_TOL
+    if boost == 8.0:
+        rows = slice(j, S) if causal else slice(0, S)
+        assert np.abs(np64(o)[0, 0, rows] - np64(v)[0, 0, j]).max() \
+            <= o_tol(dtype)
