@@ -314,6 +314,18 @@ def time_prefill(attn, inputs, torch, dev, w, steps, warmup):
     return launch_stats([e[0].elapsed_time(e[1]) for e in ev]), R
 
 
+def prefill_launch(attn, w):
+    """Kernel name, workgroups and threads per workgroup of one prefill
+    launch of workload w."""
+    if w.dtype == "f32":
+        return {"kernel": "attn_prefill_f32_kernel",
+                "workgroups": w.B * w.Hq * -(-w.S // 128), "threads": 256}
+    kern, wgs, thr = attn.prefill_workgroups(w.B, w.Hq, w.Hkv, w.S, w.D,
+                                             w.causal)
+    return {"kernel": attn.PREFILL_KERNEL_NAMES[kern], "workgroups": wgs,
+            "threads": thr}
+
+
 def prefill_record(w, st, R, traffic=None):
     """The roofline object of one prefill workload from its launch stats."""
     elt = 4 if w.dtype == "f32" else 2
@@ -322,8 +334,6 @@ def prefill_record(w, st, R, traffic=None):
     tf = flops / (st["mean_us"] * 1e-6) / 1e12
     return {
         "bound": "mfma",
-        "kernel": "attn_prefill_f32_kernel" if w.dtype == "f32"
-                  else "attn_prefill_kernel",
         "achieved": round(tf, 3),
         "peak": peak,
         "unit": "TFLOP/s",
@@ -440,7 +450,7 @@ def main():
     for w in side:
         st, R = time_prefill(attn, inputs, torch, dev, w, K, args.warmup)
         rec = prefill_record(w, st, R)
-        rec["workgroups"] = attn.prefill_workgroups(w.B, w.Hq, w.S, w.D)
+        rec.update(prefill_launch(attn, w))
         side_rec[w.name] = rec
 
     # ---- the decode as a serving loop runs it: the Rd rotated decode
@@ -475,7 +485,7 @@ def main():
     tr = measured_traffic()
     prec = prefill_record(wp, pst, Rp, traffic_for(tr, "prefill", wp.name))
     prec.pop("shape")
-    prec["workgroups"] = attn.prefill_workgroups(wp.B, wp.Hq, wp.S, wp.D)
+    prec.update(prefill_launch(attn, wp))
     d_gbs = dbytes / (dst["mean_us"] * 1e-6) / 1e9
     g_gbs = dbytes / (gst["mean_us"] * 1e-6) / 1e9
     out = {

@@ -54,6 +54,10 @@ def lib():
         L.attn_decode_workspace_size.restype = sz
         L.attn_decode_auto_splits.argtypes = [i, i]
         L.attn_decode_auto_splits.restype = i
+        L.attn_prefill_select.argtypes = [i]
+        L.attn_prefill_select.restype = i
+        L.attn_prefill_kernel_for.argtypes = [i, i, i, i, i]
+        L.attn_prefill_kernel_for.restype = i
         L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp,
                                   vp, sz, vp]
         L.attn_decode.restype = i
@@ -525,7 +529,34 @@ def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
                                lse))
 
 
-def prefill_workgroups(B, Hq, S, D):
-    """Workgroups one prefill launch uses: one per (batch, query head,
-    128-row query tile)."""
-    return B * Hq * -(-S // 128)
+PREFILL_AUTO, PREFILL_W4, PREFILL_RB = 0, 1, 2
+PREFILL_KERNEL_NAMES = {PREFILL_W4: "attn_prefill_kernel",
+                        PREFILL_RB: "attn_prefill_rb_kernel"}
+
+
+def prefill_select(kernel):
+    """Process-wide choice of the 16-bit prefill kernel (PREFILL_AUTO,
+    PREFILL_W4 or PREFILL_RB); returns the previous one."""
+    prev = int(lib().attn_prefill_select(int(kernel)))
+    if prev < 0:
+        raise ValueError(f"attn_prefill_select({kernel}): "
+                         f"{status_string(prev)}")
+    return prev
+
+
+def prefill_kernel_for(B, Hq, S, D, causal=True):
+    """PREFILL_W4 or PREFILL_RB: the kernel a 16-bit prefill launch of these
+    sizes uses under the current setting."""
+    return int(lib().attn_prefill_kernel_for(int(B), int(Hq), int(S), int(D),
+                                             int(bool(causal))))
+
+
+def prefill_workgroups(B, Hq, Hkv, S, D, causal=True):
+    """(kernel, workgroups, threads per workgroup) of one 16-bit prefill
+    launch of these sizes."""
+    kern = prefill_kernel_for(B, Hq, S, D, causal)
+    if kern == PREFILL_RB and (Hq // Hkv) % 4 == 0:
+        return kern, B * (Hq // 4) * -(-S // 64), 256
+    if kern == PREFILL_RB:
+        return kern, B * Hq * -(-S // 128), 128
+    return kern, B * Hq * -(-S // 128), 256

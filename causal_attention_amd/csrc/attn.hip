@@ -7,8 +7,6 @@
 #include <atomic>
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "decode.hpp"
 #include "kvcache.hpp"
@@ -116,35 +114,24 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-// Prefill kernel configurations for 16-bit inputs:
-//   rb: 2-wave workgroups, 64 query rows per wave (attn_prefill_rb_kernel;
-//       head dim 128 only);
-//   pp: the 8-wave ping-pong kernel (attn_prefill_pp_kernel);
-//   w4: the 4-wave kernel, two workgroups per compute unit
-//       (attn_prefill_kernel).
-// The table picks one from the shape; the environment variable
-// ATTN_PREFILL_CFG (pp | w4), read once per process, overrides it for
-// tuning sweeps.
-enum class PrefillCfg { kAuto = 0, kPP = 1, kW4 = 2, kRB = 3 };
+// Prefill kernels for 16-bit inputs:
+//   rb: attn_prefill_rb_kernel (head dim 128; one wave per SIMD, 64 query
+//       rows per wave; four query heads of a KV head per workgroup when the
+//       group size is a multiple of 4, else 2 waves of one head);
+//   w4: attn_prefill_kernel (4 waves of 32 rows, two workgroups per CU).
+// rb runs more MFMA work per cycle but in coarser workgroups; w4 balances
+// small launches better.  Measured on MI355X (causal, bf16, D = 128, group
+// sizes 1 and 4), rb is ahead once the launch holds about 5e8 score
+// elements (B Hq S^2 / 2) and behind by 5-18% below about 3e8; the table
+// switches at 4e8.  attn_prefill_select() overrides the table.
+std::atomic<int> g_prefill_kernel{ATTN_PREFILL_AUTO};
 
-PrefillCfg prefill_cfg_override() {
-  static const PrefillCfg cfg = [] {
-    const char* e = getenv("ATTN_PREFILL_CFG");
-    if (e == nullptr) return PrefillCfg::kAuto;
-    if (strcmp(e, "pp") == 0) return PrefillCfg::kPP;
-    if (strcmp(e, "w4") == 0) return PrefillCfg::kW4;
-    if (strcmp(e, "rb") == 0) return PrefillCfg::kRB;
-    return PrefillCfg::kAuto;
-  }();
-  return cfg;
-}
-
-PrefillCfg prefill_cfg(int B, int Hq, int S, int D, int causal) {
-  PrefillCfg o = prefill_cfg_override();
-  if (o == PrefillCfg::kRB && D != 128) o = PrefillCfg::kW4;
-  if (o != PrefillCfg::kAuto) return o;
-  (void)B; (void)Hq; (void)S; (void)causal;
-  return D == 128 ? PrefillCfg::kRB : PrefillCfg::kW4;
+bool prefill_use_rb(int B, int Hq, int S, int D, int causal) {
+  if (D != 128) return false;
+  const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
+  if (sel != ATTN_PREFILL_AUTO) return sel == ATTN_PREFILL_RB;
+  const double work = (double)B * Hq * S * (causal ? 0.5 * (S + 1) : S);
+  return work >= 4e8;
 }
 
 // 16-bit inputs (bf16 or fp16): the MFMA kernels for element type T.
@@ -157,27 +144,28 @@ struct Half16Prefill {
                     int S, float sl2, int nq, int ncu, int use_rope,
                     const attn::RopeRates& rope, const int* cu_seqlens,
                     const int* seq_lens) {
-      (void)b;
-      const PrefillCfg cfg = prefill_cfg(B, Hq, S, D, C);
       if constexpr (D == 128) {
-        if (cfg == PrefillCfg::kRB) {
-          hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C>), g,
-                             dim3(attn::kRBThreads), 0, st, q, k, v, o, lse,
-                             B, Hq, Hkv, S, sl2, nq, ncu, use_rope, rope,
-                             cu_seqlens, seq_lens);
+        if (prefill_use_rb(B, Hq, S, D, C)) {
+          if ((Hq / Hkv) % 4 == 0) {
+            // four query heads of a KV head per workgroup, 64-row tiles
+            const int nq4 = (S + 63) / 64;
+            hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 4>),
+                               dim3((unsigned)(B * (Hq / 4) * nq4)),
+                               dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
+                               S, sl2, nq4, ncu, use_rope, rope, cu_seqlens,
+                               seq_lens);
+          } else {
+            hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 1>), g,
+                               dim3(128), 0, st, q, k, v, o, lse, B, Hq, Hkv,
+                               S, sl2, nq, ncu, use_rope, rope, cu_seqlens,
+                               seq_lens);
+          }
           return;
         }
       }
-      if (cfg == PrefillCfg::kW4)
-        hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g,
-                           dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B,
-                           Hq, Hkv, S, sl2, nq, ncu, use_rope, rope,
-                           cu_seqlens, seq_lens);
-      else
-        hipLaunchKernelGGL((attn::attn_prefill_pp_kernel<T, D, C>), g,
-                           dim3(attn::kPPThreads), 0, st, q, k, v, o, lse, B,
-                           Hq, Hkv, S, sl2, nq, use_rope, rope, cu_seqlens,
-                           seq_lens);
+      hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st, q,
+                         k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu, use_rope,
+                         rope, cu_seqlens, seq_lens);
     }
   };
 };
@@ -560,6 +548,18 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
 }
 
 int attn_decode_auto_splits(int B, int Hkv) { return auto_splits(B, Hkv); }
+
+int attn_prefill_kernel_for(int B, int Hq, int S, int D, int causal) {
+  return prefill_use_rb(B, Hq, S, D, causal) ? ATTN_PREFILL_RB
+                                             : ATTN_PREFILL_W4;
+}
+
+int attn_prefill_select(int kernel) {
+  if (kernel != ATTN_PREFILL_AUTO && kernel != ATTN_PREFILL_W4 &&
+      kernel != ATTN_PREFILL_RB)
+    return ATTN_ERR_SHAPE;
+  return g_prefill_kernel.exchange(kernel);
+}
 
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D,
                                   int num_splits) {

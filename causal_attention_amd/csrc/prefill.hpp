@@ -566,53 +566,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   }
 }
 
-// ------------------------------------------ 8-wave ping-pong prefill kernel
-//
-// One workgroup of 8 waves per (batch, query head, 128-row query tile).  The
-// waves form two groups of four; both groups hold the same 128 query rows
-// (wave w % 4 owns rows 32 (w % 4) .. +31) and split the key tiles: group g
-// takes tiles g, g + 2, g + 4, ... (32 keys per tile at D = 128, 64 at
-// D = 64, so that each product below is 8 MFMAs).  Each group keeps its own
-// online-softmax state (the merge of key chunks of section 4.4 of the
-// attention-fusion page, done at the end through LDS).
-//
-// Waves w and w + 4 share a SIMD.  Every wave alternates compute phases
-// (8 MFMAs on operands already in registers, interleaved with softmax VALU
-// work) and load phases (LDS -> register reads of the next operand tile,
-// direct global -> LDS loads of a later tile, masking, rescaling), and the
-// two groups run one phase apart, separated by workgroup barriers: while one
-// wave of a SIMD keeps the matrix pipe busy, its partner feeds LDS and
-// memory.  Per group and key tile i (S(i) = raw scores of tile i):
-//   C0(i): S(i+1) = K(i+1) Q^T           || P(i) = exp2(x(i)), l += sum P(i)
-//   L0(i): V(i) LDS -> registers; K(i+NB) global -> LDS; mask S(i+1)
-//   C1(i): O^T += V(i)^T P(i)^T           || row max of S(i+1), reference
-//                                            max, x(i+1) = S(i+1) c - m
-//   L1(i): lazy rescale of O and l; K(i+2) LDS -> registers;
-//          V(i+NB) global -> LDS
-// The scores are double-buffered so that each compute phase has
-// independent VALU work.  K and V tiles of each group sit in a ring of NB
-// LDS slots; a slot is refilled only after every wave of its group has read
-// it, and each wave waits for its own loads of a tile before the barrier
-// that precedes the tile's first read.
-constexpr int kPPThreads = 512;
-constexpr int kPPRing = 4;                   // LDS slots per group
-
-// Block index -> (batch, KV head, query head, query tile): query tiles
-// heaviest first, consecutive blocks walking (batch, KV head) pairs first so
-// that the blocks of one pair share an XCD when the pair count divides 8.
-__device__ __forceinline__ TileCoord tile_coord_lpt(int bid, int Hq, int Hkv,
-                                                    int B, int n_qtiles) {
-  const int G = Hq / Hkv;
-  const int P = B * Hkv;
-  const int pair = bid % P;
-  const int rest = bid / P;
-  TileCoord c;
-  c.b = pair / Hkv;
-  c.g = pair % Hkv;
-  c.hq = c.g * G + rest % G;
-  c.qt = n_qtiles - 1 - rest / G;
-  return c;
-}
+// ------------------------------------------------- shared helpers
 
 // Keep a value computed before this point: the compiler otherwise sinks
 // pure arithmetic past a barrier to the phase that uses it.
@@ -621,453 +575,11 @@ __device__ __forceinline__ void pin(V& v) {
   asm volatile("" : "+v"(v));
 }
 
+// s_barrier that the scheduler moves nothing across.
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-}
-
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kPPThreads, 1) void attn_prefill_pp_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K,
-    const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
-    float scale_log2, int n_qtiles, int use_rope, RopeRates rope,
-    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
-  constexpr int BM = kPrefillBM;
-  constexpr int TK = D == 128 ? 32 : 64;      // keys per tile
-  constexpr int NSB = TK / 32;                // 32-key sub-blocks per tile
-  constexpr int KT = D / 16;                  // QK k-steps over D
-  constexpr int NDB = D / 32;                 // PV output blocks of 32 dims
-  constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;               // rows per 1 KB load
-  constexpr int TILE = TK * D * 2;            // bytes per K (or V) tile
-  constexpr int IPW = TILE / 1024 / 4;        // 1 KB loads per wave and tile
-  constexpr int NB = kPPRing;
-  constexpr int SLOT = 2 * TILE;              // K | V
-  constexpr int GROUP = NB * SLOT;            // one group's ring
-  static_assert(TILE == 8192 && IPW == 2, "8 KB tiles, 2 loads per wave");
-  static_assert(NSB * KT == 8 && NSB * 2 * NDB == 8, "8 MFMAs per phase");
-  using E = Elem16<T>;
-  typedef typename E::x8 x8;
-
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * GROUP];
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = w >> 2, wq = w & 3;
-  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const TileCoord tc = tile_coord_lpt(blockIdx.x, Hq, Hkv, B, n_qtiles);
-
-  int S = S_all;
-  size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
-  size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
-  if (cu_seqlens != nullptr) {
-    const int c0 = cu_seqlens[tc.b];
-    S = cu_seqlens[tc.b + 1] - c0;
-    if (tc.qt * BM >= S) return;           // query tile past this sequence
-    q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
-    kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
-  } else if (seq_lens != nullptr) {
-    S = min(max(seq_lens[tc.b], 0), S_all);
-  }
-  // Padding rows [S, S_all): o = 0, lse = -inf.  Group g writes the dims
-  // [g D/2, g D/2 + D/2) of a row (two 16-byte chunks per lane half).
-  auto pad_half_row = [&](int row) {
-    T* orow = O + (q_row0 + row) * D + g * (D / 2) + hh * (D / 4);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{};
-    if (LSE != nullptr && g == 0 && hh == 0) LSE[q_row0 + row] = -INFINITY;
-  };
-  const int q_lo = tc.qt * BM;
-  const int query = q_lo + 32 * wq + r;
-  if (seq_lens != nullptr && q_lo >= S) {
-    if (query < S_all) pad_half_row(query);
-    return;                                 // whole tile is padding
-  }
-  const T* Qp = Q + q_row0 * D;
-  const int q_hi = min(S, q_lo + BM);
-  const int kv_end = CAUSAL ? q_hi : S;
-  const int n_kv = (kv_end + TK - 1) / TK;
-  // Both groups run n = ceil(n_kv / 2) tiles: when n_kv is odd, group 1's
-  // last tile (index n_kv) is a dummy whose keys all lie past the range, so
-  // the mask gives it p = 0 (its loads read valid rows from the start of the
-  // sequence instead).
-  const int n = (n_kv + 1) / 2;
-  // Tiles below n_full need no mask for any row of the workgroup.
-  const int n_full = min(min(n_kv, S / TK), CAUSAL ? (q_lo + 1) / TK : n_kv);
-
-  // Q^T as the MFMA B operand: lane holds query `query`, dims 16t+8hh..+7.
-  x8 qB[KT];
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    if (query < S)
-      qB[t] = *reinterpret_cast<const x8*>(Qp + (size_t)query * D +
-                                               16 * t + 8 * hh);
-    else
-      qB[t] = x8{};
-  }
-  if (use_rope) {
-#pragma unroll
-    for (int t = 0; t < KT / 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x1 = (float)qB[t][e], x2 = (float)qB[t + KT / 2][e];
-        const double rr = hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
-        rope_pair(x1, x2, query, rr);
-        qB[t][e] = (T)x1;
-        qB[t + KT / 2][e] = (T)x2;
-      }
-  }
-
-  // Direct loads: wave wq of the group fills 1 KB blocks 2 wq, 2 wq + 1 of
-  // a tile; lane i of block b takes row b RPI + i / CPR, chunk position
-  // i % CPR, i.e. logical chunk swz(row, i % CPR).
-  // voff[ii] = byte offset of the lane's chunk in the tile minus ii KB (the
-  // immediate offset of load ii adds it back).
-  unsigned koffr[IPW], voffr[IPW];
-#pragma unroll
-  for (int ii = 0; ii < IPW; ++ii) {
-    const int row = (wq * IPW + ii) * RPI + lane / CPR, pos = lane % CPR;
-    koffr[ii] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2 - ii * 1024;
-    voffr[ii] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2 - ii * 1024;
-  }
-  const u32x4 krs = buffer_rsrc(K + kv_row0 * D);
-  const u32x4 vrs = buffer_rsrc(V + kv_row0 * D);
-  unsigned char* const gbase = smem + g * GROUP;
-  // K (kv = 0) or V (kv = 1) of this group's tile i into its ring slot.
-  auto issue = [&](int kv, int i) {
-    const int jt = 2 * i + g;
-    const int j0 = jt < n_kv ? jt * TK : 0;    // the dummy tile reads rows 0..
-    const unsigned soff = (unsigned)j0 * D * 2;
-    unsigned char* dst = gbase + (i % NB) * SLOT + kv * TILE +
-                         wq * IPW * 1024;
-    const u32x4& rs = kv ? vrs : krs;
-    if (j0 + TK <= S) {
-      lds_buffer_load16_run<IPW>(rs, kv ? voffr : koffr, soff, dst);
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < IPW; ++ii) {
-        const int row = (wq * IPW + ii) * RPI + lane / CPR;
-        const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
-        lds_buffer_load16(rs, (kv ? voffr[ii] : koffr[ii]) + ii * 1024 + back,
-                          soff, dst + ii * 1024);
-      }
-    }
-  };
-
-  // LDS operand reads.  They are plain (compiler-visible) LDS loads: the
-  // barriers are assembly statements with a memory clobber, so no read
-  // moves out of its load phase, and the compiler inserts the LDS waits
-  // before the first use.  (The direct global -> LDS loads are assembly the
-  // compiler does not see, so it never waits on them.)  Per-lane offsets
-  // from the group's ring; slot and row steps fold into the instruction's
-  // immediate offset (the swizzles repeat every 8 rows).
-  const int grp = lane >> 4, jl = lane & 15;
-  const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
-  const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
-  x8 kreg[NSB * KT];                 // K operands of the next QK
-  x8 vop[NSB * 2 * NDB];             // V operands of the next PV
-  auto read_k = [&](auto slot_c) {
-    constexpr int SL = decltype(slot_c)::value;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const int row = sb * 32 + r;
-        kreg[sb * KT + t] = *reinterpret_cast<const x8*>(
-            gbase + SL * SLOT + (row * D + 8 * swz_k<CPR>(row, 2 * t + hh)) * 2);
-      }
-  };
-  auto read_v = [&](auto slot_c) {
-    constexpr int SL = decltype(slot_c)::value;
-    const T* Vt = reinterpret_cast<const T*>(gbase + SL * SLOT + TILE);
-#pragma unroll
-    for (int su = 0; su < NSB * 2; ++su)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int row0 = su * 16 + vrow_off;
-        const int col = db * 32 + vcol_off;
-        const int c = col >> 3, e = col & 7;
-        const u32x2 lo = lds_read_tr16(Vt + row0 * D +
-                                       8 * swz_v<CPR>(row0, c) + e);
-        const u32x2 hi = lds_read_tr16(Vt + (row0 + 8) * D +
-                                       8 * swz_v<CPR>(row0 + 8, c) + e);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        vop[su * NDB + db] = __builtin_bit_cast(x8, a);
-      }
-  };
-
-  // Online-softmax state (per lane: one query row, half of each tile's
-  // keys): reference max m_ref (log2 domain, scale folded in), lane-partial
-  // sum l_i, O^T accumulators, pending rescale factor.
-  f32x16 oacc[NDB];                 // zeroed after the prologue
-  float m_ref = -INFINITY, l_i = 0.f, alpha = 1.f;
-  bool pend = false;
-  f32x16 sbuf[2][NSB];
-  x8 pP[NSB][2];
-
-  auto qk = [&](auto buf_c) {
-    constexpr int SB = decltype(buf_c)::value;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      sbuf[SB][sb] = E::mma32(kreg[sb * KT], qB[0], f32x16{});
-#pragma unroll
-      for (int t = 1; t < KT; ++t)
-        sbuf[SB][sb] = E::mma32(kreg[sb * KT + t], qB[t], sbuf[SB][sb]);
-    }
-  };
-  auto pv = [&]() {
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          oacc[db] = E::mma32(vop[(sb * 2 + uu) * NDB + db], pP[sb][uu],
-                              oacc[db]);
-        }
-  };
-  // Causal / tail mask of the raw scores of tile i (group-local index).
-  auto mask = [&](auto buf_c, int i) {
-    constexpr int SB = decltype(buf_c)::value;
-    const int j0 = (2 * i + g) * TK;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-      apply_mask_block<CAUSAL>(sbuf[SB][sb], j0 + 32 * sb, hh, query, S);
-  };
-  // Row max of tile scores, new reference when it grows by more than 2^8
-  // (valid tiles only), then x = s c - m_ref in place.
-  auto alu0 = [&](auto buf_c, bool valid) {
-    constexpr int SB = decltype(buf_c)::value;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      const f32x16& sv = sbuf[SB][sb];
-      float t0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-      float t1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
-      float t2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
-      float t3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
-      float t4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
-      mx = fmaxf(fmaxf(mx, fmaxf(fmaxf(t0, t1), t2)),
-                 fmaxf(fmaxf(t3, t4), sv[15]));
-    }
-    mx = max_halves(mx) * scale_log2;
-    const bool up = valid && (mx > m_ref + kLazyRescale);
-    const float m_new = up ? mx : m_ref;
-    alpha = up ? fast_exp2(m_ref - m_new) : alpha;
-    pend = pend || up;
-    m_ref = m_new;
-    // a row with no visible key yet keeps m_ref = -inf and gets p = 0
-    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sbuf[SB][sb][e] = fmaf(sbuf[SB][sb][e], scale_log2, neg_m);
-  };
-  auto alu1 = [&](auto buf_c) {
-    constexpr int SB = decltype(buf_c)::value;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(sbuf[SB][sb][8 * uu + e]);
-          if (e & 1) s1 += p; else s0 += p;
-          pP[sb][uu][e] = (T)p;
-        }
-    l_i += s0 + s1;
-  };
-  auto rescale = [&]() {
-    if (__ballot(pend)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      l_i *= alpha;
-      alpha = 1.f;
-      pend = false;
-    }
-  };
-  // Interleave MFMAs with the phase's softmax work.
-  auto sched_c0 = [&]() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-  };
-  auto sched_c1 = [&]() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-  };
-
-  // ---- prologue: Q (above), the first NB tiles, S(0); K(1) and V(0) in
-  // registers.  n >= 1: every query tile has a visible key.
-  for (int i = 0; i < NB && i < n; ++i) {
-    issue(0, i);
-    issue(1, i);
-  }
-  if (n >= NB) wait_vmem_le<(2 * NB - 1) * IPW>(); else wait_vmem();
-  wg_barrier();
-  read_k(std::integral_constant<int, 0>{});
-  qk(std::integral_constant<int, 0>{});
-  if (g >= n_full) mask(std::integral_constant<int, 0>{}, 0);
-  alu0(std::integral_constant<int, 0>{}, true);
-  alpha = 1.f;
-  pend = false;                      // O and l are zero: nothing to rescale
-  if (n >= NB) wait_vmem_le<(2 * NB - 3) * IPW>(); else wait_vmem();
-  wg_barrier();
-  read_k(std::integral_constant<int, 1>{});   // stale data when n == 1
-  read_v(std::integral_constant<int, 0>{});
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-
-  // ---- main loop.  Per tile i of the group (U = i % NB) a compute phase C
-  // and a load phase L; group 1 runs one phase behind group 0, so on every
-  // SIMD one wave computes while the other loads.
-  //   C(i): S(i+1) = K(i+1) Q^T || P(i) = exp2(x(i)), l += sum P(i);
-  //         [mask S(i+1)];  O^T += V(i)^T P(i)^T || row max of S(i+1),
-  //         reference, x(i+1) = S(i+1) c - m
-  //   L(i): lazy rescale; K(i+2), V(i+1) LDS -> registers;
-  //         K(i+NB), V(i+NB) global -> LDS
-  auto C = [&](auto u_c, int i) {
-    constexpr int U = decltype(u_c)::value;
-    using Bc = std::integral_constant<int, U & 1>;
-    using Bn = std::integral_constant<int, (U + 1) & 1>;
-    qk(Bn{});                                   // stale on the last tile
-    alu1(Bc{});
-    sched_c0();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      pin(pP[sb][0]);
-      pin(pP[sb][1]);
-    }
-    pin(l_i);
-    if (i + 1 < n && 2 * (i + 1) + g >= n_full) mask(Bn{}, i + 1);
-    pv();
-    alu0(Bn{}, i + 1 < n);
-    sched_c1();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) pin(sbuf[(U + 1) & 1][sb]);
-    pin(m_ref);
-    pin(alpha);
-    // K(i+2) (and the older V(i+1)) must have landed before L(i)
-    if (i + NB - 1 < n) wait_vmem_le<(2 * NB - 5) * IPW>(); else wait_vmem();
-  };
-  auto L = [&](auto u_c, int i) {
-    constexpr int U = decltype(u_c)::value;
-    rescale();
-    read_k(std::integral_constant<int, (U + 2) % NB>{});  // stale at the end
-    read_v(std::integral_constant<int, (U + 1) % NB>{});
-    if (i + NB < n) {
-      issue(0, i + NB);
-      issue(1, i + NB);
-    }
-  };
-  // Each group runs its own copy of the loop (same number of barriers).
-  auto step = [&](auto g_c, auto u_c, int it) {
-    constexpr int GG = decltype(g_c)::value;
-    constexpr int U = decltype(u_c)::value;
-    using Uc = std::integral_constant<int, U>;
-    using Up = std::integral_constant<int, (U + NB - 1) % NB>;
-    if constexpr (GG == 0) {
-      C(Uc{}, it);
-      wg_barrier();
-      L(Uc{}, it);
-      wg_barrier();
-    } else {
-      if (it > 0) L(Up{}, it - 1);
-      wg_barrier();
-      C(Uc{}, it);
-      wg_barrier();
-    }
-  };
-  static_assert(NB == 4, "the loop is unrolled by the ring size");
-  auto run_loop = [&](auto g_c) {
-    for (int it = 0; it < n; it += 4) {
-      step(g_c, std::integral_constant<int, 0>{}, it);
-      if (it + 1 < n) step(g_c, std::integral_constant<int, 1>{}, it + 1);
-      if (it + 2 < n) step(g_c, std::integral_constant<int, 2>{}, it + 2);
-      if (it + 3 < n) step(g_c, std::integral_constant<int, 3>{}, it + 3);
-    }
-  };
-  if (g == 0)
-    run_loop(std::integral_constant<int, 0>{});
-  else
-    run_loop(std::integral_constant<int, 1>{});
-  // group 1's last L is a no-op (no tile after its last), and every load
-  // has been consumed: the ring is free for the merge.
-  wait_vmem();
-  rescale();
-
-  // ---- merge the two groups' states and write O, LSE.  Group g finishes
-  // dims [g D/2, g D/2 + D/2) of its rows: it sends the other half of its
-  // accumulators (and m_ref, l) through LDS and merges what it receives.
-  constexpr int NDH = NDB / 2;
-  const float l_tot = l_i + swap_halves(l_i);
-  float2* xm = reinterpret_cast<float2*>(smem + 64 * 1024);
-  // The accumulator index must be a compile-time constant (a runtime index
-  // would move the whole array to scratch memory), so each group has its
-  // own instance of the exchange.
-  auto merge = [&](auto g_c) {
-    constexpr int GG = decltype(g_c)::value;
-    f32x4* xo = reinterpret_cast<f32x4*>(smem + GG * (32 * 1024));
-    const f32x4* xi =
-        reinterpret_cast<const f32x4*>(smem + (GG ^ 1) * (32 * 1024));
-#pragma unroll
-    for (int d = 0; d < NDH; ++d)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int db = (GG ^ 1) * NDH + d;       // the other group's half
-        xo[((wq * NDH + d) * 4 + a) * 64 + lane] =
-            f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2],
-                  oacc[db][4 * a + 3]};
-      }
-    xm[(GG * 4 + wq) * 64 + lane] = make_float2(m_ref, l_tot);
-    __syncthreads();
-    const float2 mo = xm[((GG ^ 1) * 4 + wq) * 64 + lane];
-    const float m = fmaxf(m_ref, mo.x);
-    const float a_own = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m);
-    const float a_oth = (mo.x == -INFINITY) ? 0.f : fast_exp2(mo.x - m);
-    const float L = l_tot * a_own + mo.y * a_oth;
-    if (query < S) {
-      const float inv = 1.f / L;
-      T* orow = O + (q_row0 + query) * D;
-#pragma unroll
-      for (int d = 0; d < NDH; ++d) {
-        const int db = GG * NDH + d;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 other = xi[((wq * NDH + d) * 4 + a) * 64 + lane];
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = (oacc[db][4 * a + e] * a_own + other[e] * a_oth) * inv;
-          u32x2 pr;
-          pr[0] = E::pack2(v[0], v[1]);
-          pr[1] = E::pack2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hh) = pr;
-        }
-      }
-      if (LSE != nullptr && GG == 0 && hh == 0)
-        LSE[q_row0 + query] = (m + fast_log2(L)) * kLn2;
-    } else if (seq_lens != nullptr && query < S_all) {
-      pad_half_row(query);
-    }
-  };
-  if (g == 0)
-    merge(std::integral_constant<int, 0>{});
-  else
-    merge(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------- register-blocked prefill kernel
@@ -1107,7 +619,6 @@ __global__ __launch_bounds__(kPPThreads, 1) void attn_prefill_pp_kernel(
 // The QK^T products being assembly, the wait states the hardware needs
 // between their results and a VALU read are inserted here (s_nop), with
 // margin over what the compiler emits for the same dependency.
-constexpr int kRBThreads = 128;
 constexpr int kRBRing = 4;
 constexpr int kRBMaxPasses = 8;
 // log2 headroom over the reference for probabilities of type T
@@ -1155,22 +666,31 @@ __device__ __forceinline__ void mfma_to_valu_wait(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 15\n\ts_nop 2" : "+v"(s0), "+v"(s1));
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
+// GQ = 1: one query head per workgroup, 2 waves x 64 rows (128-row query
+// tiles, two workgroups per compute unit).  GQ = 4: four query heads of one
+// KV head per workgroup, one wave per head on the same 64 rows (64-row
+// query tiles, one workgroup per compute unit): every K / V tile loaded
+// into LDS feeds 256 query rows instead of 128, and all waves share one
+// causal diagonal.
+template <typename T, int D, bool CAUSAL, int GQ>
+__global__ __launch_bounds__(GQ == 4 ? 256 : 128, GQ == 4 ? 1 : 2)
+void attn_prefill_rb_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
     float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
     const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
   static_assert(D == 128, "64 rows per wave at head dim 128");
-  constexpr int BM = kPrefillBM;              // 128 rows per workgroup
+  static_assert(GQ == 1 || GQ == 4, "heads per workgroup");
+  constexpr int WAVES = GQ == 4 ? 4 : 2;
+  constexpr int BM = GQ == 4 ? 64 : 128;      // query rows per head
   constexpr int TK = 32;                      // keys per tile
   constexpr int KT = D / 16;                  // QK k-steps
   constexpr int NDB = D / 32;                 // PV output blocks
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;               // rows per 1 KB load
   constexpr int TILE = TK * D * 2;            // 8 KB per K (or V) tile
-  constexpr int IPW = TILE / 1024 / 2;        // 4 loads per wave and tile
+  constexpr int IPW = TILE / 1024 / WAVES;    // loads per wave and tile
   constexpr int NB = kRBRing;
   constexpr int SLOT = 2 * TILE;
   using E = Elem16<T>;
@@ -1182,17 +702,19 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  // (batch, KV head, head group, query tile); this wave's query head
   const TileCoord tc =
-      tile_coord(blockIdx.x, gridDim.x, B, Hq, Hkv, n_qtiles, n_cu);
+      tile_coord(blockIdx.x, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, n_cu);
+  const int hq = tc.hq * GQ + (GQ == 4 ? w : 0);
 
   int S = S_all;
-  size_t q_row0 = (size_t)(tc.b * Hq + tc.hq) * S_all;
+  size_t q_row0 = (size_t)(tc.b * Hq + hq) * S_all;
   size_t kv_row0 = (size_t)(tc.b * Hkv + tc.g) * S_all;
   if (cu_seqlens != nullptr) {
     const int c0 = cu_seqlens[tc.b];
     S = cu_seqlens[tc.b + 1] - c0;
     if (tc.qt * BM >= S) return;
-    q_row0 = (size_t)c0 * Hq + (size_t)tc.hq * S;
+    q_row0 = (size_t)c0 * Hq + (size_t)hq * S;
     kv_row0 = (size_t)c0 * Hkv + (size_t)tc.g * S;
   } else if (seq_lens != nullptr) {
     S = min(max(seq_lens[tc.b], 0), S_all);
@@ -1206,7 +728,7 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
     if (LSE != nullptr && hh == 0) LSE[q_row0 + row] = -INFINITY;
   };
   const int q_lo = tc.qt * BM;
-  const int wq0 = q_lo + 64 * w;              // first row of this wave
+  const int wq0 = q_lo + (GQ == 4 ? 0 : 64 * w);   // first row of this wave
   if (seq_lens != nullptr && q_lo >= S) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -1246,7 +768,7 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
     for (int t = 0; t < KT; ++t) qB[rb][t] = __builtin_bit_cast(u32x4, qv[t]);
   }
 
-  // Direct loads: wave w fills 1 KB blocks 4w .. 4w+3 of a tile.
+  // Direct loads: wave w fills 1 KB blocks IPW w .. IPW w + IPW-1 of a tile.
   unsigned koffr[IPW], voffr[IPW];
 #pragma unroll
   for (int ii = 0; ii < IPW; ++ii) {
@@ -1287,7 +809,7 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
   };
 
   u32x4 kreg[KT];                      // K operands of the next QK
-  u32x4 vop[2 * NDB];                  // V operands of the next PV
+  u32x4 vop[2][2 * NDB];               // V operands, double-buffered
   const int grp = lane >> 4, jl = lane & 15;
   const int vrow_off = 4 * (grp >> 1) + (jl >> 2);
   const int vcol_off = 16 * (grp & 1) + 4 * (jl & 3);
@@ -1296,22 +818,19 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
     kreg[t] = *reinterpret_cast<const u32x4*>(
         smem + SL * SLOT + (r * D + 8 * swz_k<CPR>(r, 2 * t + hh)) * 2);
   };
-  auto read_v = [&](auto slot_c) {
+  // Half h (keys 8h .. 8h+7 of its k-step) of V operand x (k-step x / NDB,
+  // output block x % NDB) of slot SL.
+  auto read_vh = [&](auto slot_c, auto buf_c, int x, int h) {
     constexpr int SL = decltype(slot_c)::value;
+    constexpr int VB = decltype(buf_c)::value;
     const T* Vt = reinterpret_cast<const T*>(smem + SL * SLOT + TILE);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int row0 = u * 16 + vrow_off;
-        const int col = db * 32 + vcol_off;
-        const int c = col >> 3, e = col & 7;
-        const u32x2 lo = lds_read_tr16(Vt + row0 * D +
-                                       8 * swz_v<CPR>(row0, c) + e);
-        const u32x2 hi = lds_read_tr16(Vt + (row0 + 8) * D +
-                                       8 * swz_v<CPR>(row0 + 8, c) + e);
-        vop[u * NDB + db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
+    const int u = x / NDB, db = x % NDB;
+    const int row = u * 16 + vrow_off + 8 * h;
+    const int col = db * 32 + vcol_off;
+    const int c = col >> 3, e = col & 7;
+    const u32x2 v = lds_read_tr16(Vt + row * D + 8 * swz_v<CPR>(row, c) + e);
+    vop[VB][x][2 * h] = v[0];
+    vop[VB][x][2 * h + 1] = v[1];
   };
 
   f32x16 oacc[2][NDB];
@@ -1377,18 +896,19 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
   // max in pass 0, the bound computed after the previous pass otherwise.
   using B0 = std::integral_constant<int, 0>;
   auto run_pass = [&](int pass, const float (&m_next)[2]) {
-    // ---- prologue: K0 K1 K2 V0 K3 V1 V2 in flight, then S(0), then K4
-    // into K0's slot; K(1) in registers.  From here on tile t loads K(t+5)
-    // and V(t+3) (every load is issued, past the end too, so the counts of
-    // loads in flight are fixed).
+    // ---- prologue: K0 K1 V0 K2 V1 K3 V2 V3 in flight, then S(0), then K4
+    // into K0's slot; K(1) and V(0) in registers.  From here on tile t
+    // loads K(t+5) and V(t+4) (every load is issued, past the end too, so
+    // the counts of loads in flight are fixed).
     issue(0, 0);
     issue(0, 1);
-    issue(0, 2);
     issue(1, 0);
-    issue(0, 3);
+    issue(0, 2);
     issue(1, 1);
+    issue(0, 3);
     issue(1, 2);
-    wait_vmem_le<6 * IPW>();                  // K0
+    issue(1, 3);
+    wait_vmem_le<7 * IPW>();                  // K0
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < KT; ++t) read_k1(B0{}, t);
@@ -1408,10 +928,15 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
       for (int e0 = 0; e0 < 16; e0 += 4) fma4(B0{}, rb, e0, -m_ref[rb]);
       l_i[rb] = 0.f;
     }
-    // the first tile reads K(1) now, V(0) and K(2) next
-    wait_vmem_le<3 * IPW>();                  // K1, K2, V0
+    // K(1), V(0) now; K(2), V(1) in the first tile
+    wait_vmem_le<3 * IPW>();                  // K1, V0, K2, V1
     __syncthreads();
     issue(0, 4);
+#pragma unroll
+    for (int x = 0; x < 2 * NDB; ++x) {
+      read_vh(B0{}, B0{}, x, 0);
+      read_vh(B0{}, B0{}, x, 1);
+    }
 #pragma unroll
     for (int t = 0; t < KT; ++t)
       read_k1(std::integral_constant<int, 1>{}, t);   // stale when n == 1
@@ -1432,12 +957,13 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
       constexpr bool MASKED = decltype(masked_c)::value;
       using Bc = std::integral_constant<int, U & 1>;
       using Bn = std::integral_constant<int, (U + 1) & 1>;
-      using Sv = std::integral_constant<int, U>;
+      using Vn = std::integral_constant<int, (U + 1) & 1>;
+      using Sv = std::integral_constant<int, (U + 1) % NB>;
       using Sk = std::integral_constant<int, (U + 2) % NB>;
-      // A(i): V(i) reads; 16 QK MFMAs of S(i+1), each followed by the
-      // exponentials of one pair of scores of tile i and the packing of the
-      // previous pair, every other one by a load of K(i+5) or V(i+3).
-      read_v(Sv{});
+      // A(i): 16 QK MFMAs of S(i+1), each followed by the exponentials of
+      // one pair of scores of tile i and the packing of the previous pair;
+      // 2 IPW evenly spaced ones also by this wave's loads of K(i+5) and
+      // V(i+4).
       float pe0, pe1;
       exp_pair(Bc{}, 0, pe0, pe1);
       static_for<16>([&](auto s_c) {
@@ -1449,12 +975,13 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
         use_pair(s, pe0, pe1);
         pe0 = ne0;
         pe1 = ne1;
-        if constexpr ((s & 1) != 0) {
-          constexpr int q = s >> 1;
+        constexpr int GAP = 16 / (2 * IPW);     // slots per load
+        if constexpr (s % GAP == GAP - 1) {
+          constexpr int q = s / GAP;
           if constexpr (q < IPW)
             issue1(0, i + 5, std::integral_constant<int, q>{}, full_c);
           else
-            issue1(1, i + 3, std::integral_constant<int, q - IPW>{}, full_c);
+            issue1(1, i + 4, std::integral_constant<int, q - IPW>{}, full_c);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -1464,21 +991,25 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
         pin(pP[rb][0]);
         pin(pP[rb][1]);
       }
-      // B(i): 16 PV MFMAs, each followed by a slice of the row sums of P(i),
-      // of the K(i+2) reads, of the mask of S(i+1) (tiles that need one) and
-      // of x(i+1) = S(i+1) c - m.
+      // B(i): 16 PV MFMAs (V operands read in the previous tile), each
+      // followed by a slice of the row sums of P(i), of the mask of S(i+1)
+      // (tiles that need one) and of x(i+1) = S(i+1) c - m, by one of the
+      // V(i+1) operand reads, every other one by one of the K(i+2) reads
+      // (LDS reads spread evenly: bunched, the four waves' reads exceed the
+      // LDS bandwidth and stall issue).
       const float nm0 = -m_ref[0], nm1 = -m_ref[1];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int u = k >> 3, db = (k >> 1) & 3, rb = k & 1;
-        oacc[rb][db] = E::mma32(__builtin_bit_cast(x8, vop[u * NDB + db]),
+        oacc[rb][db] = E::mma32(__builtin_bit_cast(x8, vop[U & 1][u * NDB + db]),
                                 __builtin_bit_cast(x8, pP[rb][u]),
                                 oacc[rb][db]);
         __builtin_amdgcn_sched_barrier(0);
         // S(i+1) complete (the wait overlaps this MFMA)
         if (k == 0) mfma_to_valu_wait(sbuf[(U + 1) & 1][0],
                                       sbuf[(U + 1) & 1][1]);
-        if (k < KT) read_k1(Sk{}, k);          // stale at the end
+        if (k % 2 == 0) read_k1(Sk{}, k / 2);  // stale at the end
+        read_vh(Sv{}, Vn{}, k >> 1, k & 1);     // stale at the end
         sum_pair(Bc{}, k);
         if constexpr (MASKED) {
           if (k >= 1 && k < 9) {
@@ -1503,9 +1034,9 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
         pin(sbuf[(U + 1) & 1][rb]);
       }
       // Before the barrier: this wave's loads of the tiles read next
-      // (V(i+1), K(i+3), issued two tiles ago; the loads of the last two
-      // tiles may still run) have landed and its LDS reads of tile i are
-      // complete; after it, the slots of V(i) and K(i+2) may be refilled.
+      // (V(i+2), K(i+3), issued two tiles ago; the loads of the last two
+      // tiles may still run) have landed and its LDS reads of V(i+1) and
+      // K(i+2) are complete; after it, their slots may be refilled.
       wait_vmem_le<4 * IPW>();
       __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
       wg_barrier();
@@ -1562,7 +1093,10 @@ __global__ __launch_bounds__(kRBThreads, 2) void attn_prefill_rb_kernel(
     const int any = __ballot(over) != 0;      // with every lane active
     if (lane == 0) flag[w] = any;
     __syncthreads();
-    const bool again = (flag[0] | flag[1]) != 0;
+    int any_w = 0;
+#pragma unroll
+    for (int x = 0; x < WAVES; ++x) any_w |= flag[x];
+    const bool again = any_w != 0;
     __syncthreads();
     if (!again) break;
   }

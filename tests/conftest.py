@@ -27,3 +27,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(params=["w4", "rb"])
+def prefill_kernel(request):
+    """Runs a prefill test once under each 16-bit prefill kernel (the
+    register-blocked one applies to head dim 128; at D = 64 both runs use
+    the 4-wave kernel) and restores the automatic choice afterwards."""
+    from causal_attention_amd import attn
+    prev = attn.prefill_select({"w4": attn.PREFILL_W4,
+                                "rb": attn.PREFILL_RB}[request.param])
+    yield request.param
+    attn.prefill_select(prev)

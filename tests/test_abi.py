@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
               "attn_prefill_padded_f16", "attn_kv_append_f16",
               "attn_decode_padded_f16", "attn_decode_noalloc",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
+              "attn_prefill_select", "attn_prefill_kernel_for",
               "attn_status_string"]:
         assert n in names
 
@@ -45,6 +46,37 @@ def test_status_strings():
     for code, name in attn.STATUS.items():
         assert attn.status_string(code) == name
     assert attn.status_string(-99) == "ATTN_ERR_UNKNOWN"
+
+
+def test_prefill_kernel_selection():
+    # host-only: the setting and the shape table, no launch
+    W4, RB = attn.PREFILL_W4, attn.PREFILL_RB
+    assert attn.lib().attn_prefill_select(7) == -2      # rejected, unchanged
+    prev = attn.prefill_select(attn.PREFILL_AUTO)
+    try:
+        # automatic: head dim 64 always W4; D = 128 by the launch's work
+        assert attn.prefill_kernel_for(1, 8, 32768, 64) == W4
+        assert attn.prefill_kernel_for(1, 8, 32768, 128) == RB
+        assert attn.prefill_kernel_for(4, 8, 2048, 128) == W4
+        assert attn.prefill_kernel_for(1, 8, 32768, 128, causal=False) == RB
+        assert attn.prefill_select(RB) == attn.PREFILL_AUTO
+        assert attn.prefill_kernel_for(1, 1, 1, 128) == RB
+        assert attn.prefill_kernel_for(1, 1, 1, 64) == W4
+        assert attn.prefill_select(W4) == RB
+        assert attn.prefill_kernel_for(1, 8, 32768, 128) == W4
+        # launch geometry
+        attn.prefill_select(RB)
+        assert attn.prefill_workgroups(2, 8, 2, 1000, 128) == (RB, 2 * 2 * 16,
+                                                              256)
+        assert attn.prefill_workgroups(2, 6, 3, 1000, 128) == (RB, 2 * 6 * 8,
+                                                              128)
+        attn.prefill_select(W4)
+        assert attn.prefill_workgroups(2, 8, 2, 1000, 128) == (W4, 2 * 8 * 8,
+                                                              256)
+        with pytest.raises(ValueError):
+            attn.prefill_select(3)
+    finally:
+        attn.prefill_select(prev)
 
 
 def prefill(fn="attn_prefill", q=A, k=A, v=A, o=A, lse=A, B=1, Hq=8, Hkv=2,

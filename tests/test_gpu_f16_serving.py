@@ -205,6 +205,7 @@ def test_decode_step_graph_replay_f16(rope_base):
 @pytest.mark.parametrize("B,Hq,Hkv,S,D", [(1, 8, 2, 300, 128),
                                           (2, 12, 12, 129, 64)])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_rope_f16_matches_oracle(B, Hq, Hkv, S, D, causal):
     base = 10000.0
     say(f"[prefill rope f16] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} "
@@ -225,6 +226,7 @@ def test_prefill_rope_f16_matches_oracle(B, Hq, Hkv, S, D, causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_varlen_f16_matches_oracle(causal):
     lens, Hq, Hkv, D = [0, 1, 127, 129, 1000, 257], 8, 2, 128
     say(f"[prefill varlen f16] lens={lens} causal={causal}")
@@ -247,6 +249,7 @@ def test_prefill_varlen_f16_matches_oracle(causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_padded_f16_matches_oracle(causal):
     B, Hq, Hkv, S, D, lens = 4, 8, 2, 257, 128, [129, 0, 200, 257]
     say(f"[prefill padded f16] lens={lens} causal={causal}")

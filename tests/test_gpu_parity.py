@@ -89,11 +89,13 @@ def test_c2_mha12_s512():
     check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_c3_gqa_b4_s2048():
     w = inputs.WORKLOADS["c3_gqa_b4_s2048"]
     check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_c5_long_context_sampled_rows():
     w = inputs.WORKLOADS["c5_gqa_s32768"]
     q, k, v, o, lse, scale = run_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype,
@@ -122,6 +124,7 @@ def _randn_bf16(shape, seed):
     return torch.randn(shape, generator=g, device=DEV, dtype=torch.bfloat16)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_offsets_beyond_4gb_sampled():
     """Tensors past 2^31 elements (q, o: 4.4 GB): the last (batch, head)
     pairs, whose rows start beyond element 2^31, are checked row by row
@@ -187,6 +190,7 @@ def test_decode_cache_beyond_4gb_sampled():
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (12, 12), (8, 2), (8, 1)])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_edge_shapes_bf16(S, D, Hq, Hkv, causal):
     check_prefill(2 if S < 200 else 1, Hq, Hkv, S, D, "bf16", causal,
                   seed=S + D)
@@ -201,10 +205,12 @@ def test_prefill_edge_shapes_f32(S, D, causal):
 
 @pytest.mark.parametrize("sigma", [0.01, 1.0, 4.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_value_scale_sweep(sigma, dtype):
     check_prefill(1, 8, 2, 257, 128, dtype, True, sigma=sigma, seed=7)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_is_deterministic():
     w = inputs.WORKLOADS["c3_gqa_b4_s2048"]
     q, k, v = (t.to(DEV) for t in
@@ -215,6 +221,7 @@ def test_prefill_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_without_lse():
     q, k, v = (t.to(DEV) for t in
                inputs.prefill_inputs(1, 8, 2, 100, 128, "bf16", 1.0, 4))
@@ -328,6 +335,7 @@ def test_decode_split_count_changes_only_rounding():
             assert (lse - ref[1]).abs().max() <= 1e-4
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_decode_equals_last_prefill_row():
     Hq, Hkv, D, L = 8, 2, 128, 333
     q, k, v = inputs.prefill_inputs(1, Hq, Hkv, L, D, "bf16", 1.0, 21)
@@ -377,15 +385,18 @@ def test_decode_is_deterministic():
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (8, 2)])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_edge_shapes_f16(S, D, Hq, Hkv, causal):
     check_prefill(1, Hq, Hkv, S, D, "f16", causal)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_c3_shape_f16():
     check_prefill(4, 8, 2, 2048, 128, "f16", True)
 
 
 @pytest.mark.parametrize("sigma", [0.01, 4.0])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_value_scale_f16(sigma):
     check_prefill(1, 8, 2, 300, 128, "f16", True, sigma=sigma)
 
@@ -547,6 +558,7 @@ def test_decode_step_graph_replay(rope_base):
         assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_graph_replay():
     """A prefill launch captured once in a graph and replayed with new
     inputs copied in between: every replay equals an eager launch on the
@@ -600,6 +612,7 @@ def test_prefill_graph_replay():
     (2, 8, 1, 1000, 128, [999, 333]),
 ])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_padded_matches_oracle(B, Hq, Hkv, S, D, lens, causal):
     say(f"[prefill padded] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} lens={lens} "
         f"causal={causal}")
@@ -620,6 +633,7 @@ def test_prefill_padded_matches_oracle(B, Hq, Hkv, S, D, lens, causal):
             assert eo <= o_tol("bf16") and el <= LSE_TOL
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_padded_full_lengths_equal_dense_and_ignore_padding():
     # lengths = S: the dense kernel's results bit for bit; and values written
     # into the padding rows change nothing
@@ -649,6 +663,7 @@ def test_prefill_padded_full_lengths_equal_dense_and_ignore_padding():
                                           (1, 1, 1, 1, 128),
                                           (4, 8, 2, 2048, 128)])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_rope_matches_oracle(B, Hq, Hkv, S, D, causal):
     base = 10000.0
     say(f"[prefill rope] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal}")
@@ -668,6 +683,7 @@ def test_prefill_rope_matches_oracle(B, Hq, Hkv, S, D, causal):
     assert eo <= 2e-2 and el <= LSE_TOL
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_rope_long_positions_sampled():
     """Angles at positions up to 8191: reduced in fp64, so late rows are as
     accurate as early ones.  Sampled rows against the oracle."""
@@ -726,6 +742,7 @@ def packed_inputs(lens, Hq, Hkv, D, seed):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (1, 1)])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_varlen_matches_oracle(D, Hq, Hkv, causal):
     lens = [0, 1, 127, 128, 129, 1000, 257]
     say(f"[prefill varlen] lens={lens} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
@@ -741,6 +758,7 @@ def test_prefill_varlen_matches_oracle(D, Hq, Hkv, causal):
     assert eo <= 2e-2 and el <= LSE_TOL
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_varlen_equal_lengths_is_the_dense_kernel():
     # with equal lengths the packed layout is [B, H, S, D]; every workgroup
     # does the same arithmetic as the dense launch, so the results match
@@ -762,6 +780,7 @@ def test_prefill_varlen_equal_lengths_is_the_dense_kernel():
 @pytest.mark.parametrize("boost", [8.0, 1.5])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_late_dominant_key(dtype, causal, boost):
     """One late key aligned with every query row of head 0 and `boost` times
     as long.  boost 8: its score exceeds each row's first-tile maximum by
