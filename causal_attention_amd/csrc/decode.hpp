@@ -25,10 +25,14 @@
 //    per piece, and the range holding its first block records which ranges
 //    hold the others, for the combine kernel.
 //  * Each wave streams its blocks in order through a double-buffered LDS
-//    ring: K, V and the segment's G query rows arrive by gfx950's direct
-//    loads (global_load_lds_dwordx4, 1 KB contiguous per instruction), and
-//    the next block's loads (across segment ends too) are issued before the
-//    current one is multiplied.
+//    ring: K and V (and, with a piece's first block, the segment's G query
+//    rows) arrive by gfx950's direct loads (global_load_lds_dwordx4, 1 KB
+//    contiguous per instruction), and the next block's loads (across
+//    segment ends too) are issued before the current one is multiplied.
+//    A deeper ring (four buffers) measured no faster: the kernel streams
+//    at about 5.7 TB/s once running, and its time on the C4 workload is
+//    dominated by the fixed latency of a launch (length scan, first load,
+//    tail), not by loads in flight.
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (_f16 for
 //    fp16 inputs; the heads are MFMA columns, the other columns are zero):
 //    K rows are the A operand, V^T comes from transposed LDS reads
@@ -315,11 +319,15 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
         dec_lds_load16(Vb + voff[i], kb + KBYTES + i * 1024);
       }
     }
-    const char* Qp = reinterpret_cast<const char*>(
-        Q + ((size_t)s.b * Hq + (size_t)s.g * G) * D);
+    // the query rows only with a piece's first block (compute reads them
+    // there once and keeps them in registers)
+    if (blk == s.a) {
+      const char* Qp = reinterpret_cast<const char*>(
+          Q + ((size_t)s.b * Hq + (size_t)s.g * G) * D);
 #pragma unroll
-    for (int i = 0; i < NQI; ++i)
-      dec_lds_load16(Qp + qoff[i], kb + 2 * KBYTES + i * 1024);
+      for (int i = 0; i < NQI; ++i)
+        dec_lds_load16(Qp + qoff[i], kb + 2 * KBYTES + i * 1024);
+    }
   };
 
   // Online-softmax state of head c16: reference max (log2 domain),
@@ -468,10 +476,10 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
     l_i = 0.f;
     for (long long blk = cur.a; blk < cur.e; ++blk) {
       if (blk + 1 < cur.e) {
-        issue(cur, blk + 1, (n + 1) & 1);
-        wait_vmem_le<Lay::GROUP>();
+        issue(cur, blk + 1, (n + 1) & 1);     // not a piece's first block
+        wait_vmem_le<2 * NKI>();
       } else if (nxt.valid) {
-        issue(nxt, nxt.a, (n + 1) & 1);
+        issue(nxt, nxt.a, (n + 1) & 1);       // K, V and the query rows
         wait_vmem_le<Lay::GROUP>();
       } else {
         wait_vmem_le<0>();

@@ -993,10 +993,8 @@ void attn_prefill_rb_kernel(
       }
       // B(i): 16 PV MFMAs (V operands read in the previous tile), each
       // followed by a slice of the row sums of P(i), of the mask of S(i+1)
-      // (tiles that need one) and of x(i+1) = S(i+1) c - m, by one of the
-      // V(i+1) operand reads, every other one by one of the K(i+2) reads
-      // (LDS reads spread evenly: bunched, the four waves' reads exceed the
-      // LDS bandwidth and stall issue).
+      // (tiles that need one) and of x(i+1) = S(i+1) c - m; the first eight
+      // by the V(i+1) operand reads, slots 4 .. 11 by the K(i+2) reads.
       const float nm0 = -m_ref[0], nm1 = -m_ref[1];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -1008,8 +1006,13 @@ void attn_prefill_rb_kernel(
         // S(i+1) complete (the wait overlaps this MFMA)
         if (k == 0) mfma_to_valu_wait(sbuf[(U + 1) & 1][0],
                                       sbuf[(U + 1) & 1][1]);
-        if (k % 2 == 0) read_k1(Sk{}, k / 2);  // stale at the end
-        read_vh(Sv{}, Vn{}, k >> 1, k & 1);     // stale at the end
+        // LDS reads end by slot 11, so that the wait for them before the
+        // barrier finds them done
+        if (k < 8) {
+          read_vh(Sv{}, Vn{}, k, 0);            // stale at the end
+          read_vh(Sv{}, Vn{}, k, 1);
+        }
+        if (k >= 4 && k < 12) read_k1(Sk{}, k - 4);   // stale at the end
         sum_pair(Bc{}, k);
         if constexpr (MASKED) {
           if (k >= 1 && k < 9) {
