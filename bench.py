@@ -360,7 +360,8 @@ def main():
     ap.add_argument("--prefill", default="c5_gqa_s32768",
                     help="prefill workload of the step (value / roofline)")
     ap.add_argument("--decode", default="c4_decode_b32")
-    ap.add_argument("--side", default="c3_gqa_b4_s2048",
+    ap.add_argument("--side",
+                    default="c3_gqa_b4_s2048,c2_mha12_s512,c1_f32_s128",
                     help="comma-separated prefill workloads timed after the "
                     "step, reported under side_configs ('' for none)")
     ap.add_argument("--num-splits", type=int, default=0)
