@@ -328,8 +328,13 @@ def prefill_launch(attn, w):
                 "workgroups": w.B * w.Hq * -(-w.S // 128), "threads": 256}
     kern, wgs, thr = attn.prefill_workgroups(w.B, w.Hq, w.Hkv, w.S, w.D,
                                              w.causal)
+    balanced = attn.prefill_balanced(w.B, w.Hq, w.Hkv, w.S, w.D, w.causal)
     return {"kernel": attn.PREFILL_KERNEL_NAMES[kern], "workgroups": wgs,
-            "threads": thr}
+            "threads": thr,
+            "schedule": ("balanced: query tiles t and n-1-t paired, each "
+                         "pair's key tiles cut evenly between two "
+                         "workgroups" if balanced else
+                         "one workgroup per query tile, heaviest first")}
 
 
 def prefill_record(w, st, R, traffic=None):

@@ -50,6 +50,15 @@ def lib():
         L.attn_prefill_f16.restype = i
         L.attn_prefill_f32.argtypes = L.attn_prefill.argtypes
         L.attn_prefill_f32.restype = i
+        L.attn_prefill_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f,
+                                      i, vp, sz, vp]
+        L.attn_prefill_ws.restype = i
+        L.attn_prefill_ws_f16.argtypes = L.attn_prefill_ws.argtypes
+        L.attn_prefill_ws_f16.restype = i
+        L.attn_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
+        L.attn_prefill_workspace_size.restype = sz
+        L.attn_prefill_split_wait.argtypes = [i]
+        L.attn_prefill_split_wait.restype = i
         L.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
         L.attn_decode_workspace_size.restype = sz
         L.attn_decode_auto_splits.argtypes = [i, i]
@@ -164,14 +173,80 @@ def _lse_arg(lse, with_lse, shape, like):
     return lse
 
 
+_PREFILL_WS_FN = {torch.bfloat16: "attn_prefill_ws",
+                  torch.float16: "attn_prefill_ws_f16"}
+_prefill_ws_on = True
+_prefill_ws_cache = {}
+
+
+def attn_prefill_workspace_size(B, Hq, Hkv, S, D, causal=True):
+    """Bytes of workspace that enable the balanced causal schedule of a
+    16-bit prefill of these sizes on the current device (0: none)."""
+    return int(lib().attn_prefill_workspace_size(
+        int(B), int(Hq), int(Hkv), int(S), int(D), int(bool(causal))))
+
+
+def prefill_workspace_policy(on):
+    """Whether ``attn_prefill`` and ``prepare_prefill`` pass a workspace to
+    16-bit launches (the default) or call the plain entry points; returns
+    the previous setting."""
+    global _prefill_ws_on
+    prev, _prefill_ws_on = _prefill_ws_on, bool(on)
+    return prev
+
+
+def prefill_split_wait(ticks):
+    """Bound of the balanced schedule's wait for a partner's part, in ticks
+    of the 100 MHz GPU real-time counter (-1: the kernel's own rule, 0: give
+    up at once); returns the previous setting."""
+    prev = int(lib().attn_prefill_split_wait(int(ticks)))
+    if prev < -1:
+        raise ValueError(f"attn_prefill_split_wait({ticks}): "
+                         f"{status_string(prev)}")
+    return prev
+
+
+def new_prefill_workspace(B, Hq, Hkv, S, D, causal=True, device="cuda"):
+    """A zeroed workspace for ``attn_prefill(..., workspace=)`` (uint8; at
+    least one byte, so that it can be passed where none is needed)."""
+    n = max(1, attn_prefill_workspace_size(B, Hq, Hkv, S, D, causal))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _prefill_workspace(q, B, Hq, Hkv, S, D, causal, workspace=None):
+    """The workspace for one 16-bit prefill, or None: the caller's, else one
+    zero-filled once and kept per (device, stream), so that calls sharing
+    one never overlap (the library leaves its flag words zero after every
+    call)."""
+    if q.dtype not in _PREFILL_WS_FN:
+        return None
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, 1)
+        return workspace
+    if not _prefill_ws_on:
+        return None
+    nbytes = attn_prefill_workspace_size(B, Hq, Hkv, S, D, causal)
+    if nbytes == 0:
+        return None
+    key = (q.device.index, torch.cuda.current_stream(q.device).cuda_stream)
+    ws = _prefill_ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+        _prefill_ws_cache[key] = ws
+    return ws
+
+
 def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
-                 with_lse=True):
+                 with_lse=True, workspace=None):
     """Fused prefill attention.
 
-    q [B,Hq,S,D]; k, v [B,Hkv,S,D]; bf16 (calls ``attn_prefill``), fp16
-    (``attn_prefill_f16``) or fp32 (``attn_prefill_f32``).  Returns (o, lse)
+    q [B,Hq,S,D]; k, v [B,Hkv,S,D]; bf16 (calls ``attn_prefill_ws`` or
+    ``attn_prefill``), fp16 (``attn_prefill_ws_f16`` or
+    ``attn_prefill_f16``) or fp32 (``attn_prefill_f32``).  Returns (o, lse)
     with o like q and lse fp32 [B,Hq,S] (None when ``with_lse`` is False).
-    ``scale`` defaults to 1/sqrt(D).
+    ``scale`` defaults to 1/sqrt(D).  16-bit launches get a workspace:
+    ``workspace`` (uint8, from ``new_prefill_workspace``) if given, else one
+    kept per stream unless ``prefill_workspace_policy(False)`` is set.
     """
     dtype = q.dtype
     if dtype not in _PREFILL_FN:
@@ -184,12 +259,21 @@ def attn_prefill(q, k, v, causal=True, scale=None, out=None, lse=None,
     _check(out, "out", dtype, 4)
     _shape(out, "out", q.shape)
     lse = _lse_arg(lse, with_lse, (B, Hq, S), q)
-    _on_gpu(q=q, k=k, v=v, out=out, lse=lse)
-    fn = getattr(lib(), _PREFILL_FN[dtype])
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
+    _on_gpu(q=q, k=k, v=v, out=out, lse=lse, workspace=workspace)
+    ws = _prefill_workspace(q, B, Hq, Hkv, S, D, causal, workspace)
+    if ws is not None:
+        name = _PREFILL_WS_FN[dtype]
+        st = getattr(lib(), name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
+            D, float(scale), int(bool(causal)), _ptr(ws), ws.numel(),
+            _stream())
+    else:
+        name = _PREFILL_FN[dtype]
+        st = getattr(lib(), name)(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
             D, float(scale), int(bool(causal)), _stream())
     if st != 0:
-        raise AttnError(st, _PREFILL_FN[dtype])
+        raise AttnError(st, name)
     return out, lse
 
 
@@ -491,10 +575,18 @@ def prepare_prefill(q, k, v, out, lse=None, causal=True, scale=None):
     _on_gpu(q=q, k=k, v=v, out=out, lse=lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    fn = getattr(lib(), _PREFILL_FN[dtype])
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S,
-            D, ctypes.c_float(scale), int(bool(causal)), _stream())
-    return PreparedCall(fn, _PREFILL_FN[dtype], args, (q, k, v, out, lse))
+    ws = _prefill_workspace(q, B, Hq, Hkv, S, D, causal)
+    if ws is not None:
+        name = _PREFILL_WS_FN[dtype]
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                S, D, ctypes.c_float(scale), int(bool(causal)), _ptr(ws),
+                ws.numel(), _stream())
+    else:
+        name = _PREFILL_FN[dtype]
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                S, D, ctypes.c_float(scale), int(bool(causal)), _stream())
+    return PreparedCall(getattr(lib(), name), name, args,
+                        (q, k, v, out, lse, ws))
 
 
 def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
@@ -551,9 +643,18 @@ def prefill_kernel_for(B, Hq, S, D, causal=True):
                                              int(bool(causal))))
 
 
+def prefill_balanced(B, Hq, Hkv, S, D, causal=True):
+    """Whether a 16-bit ``attn_prefill`` of these sizes runs the balanced
+    causal schedule (a workspace is passed and the schedule applies)."""
+    return _prefill_ws_on and attn_prefill_workspace_size(
+        B, Hq, Hkv, S, D, causal) > 0
+
+
 def prefill_workgroups(B, Hq, Hkv, S, D, causal=True):
     """(kernel, workgroups, threads per workgroup) of one 16-bit prefill
-    launch of these sizes."""
+    launch of these sizes through ``attn_prefill``."""
+    if prefill_balanced(B, Hq, Hkv, S, D, causal):
+        return PREFILL_RB, B * (Hq // 4) * -(-S // 64), 256
     kern = prefill_kernel_for(B, Hq, S, D, causal)
     if kern == PREFILL_RB and (Hq // Hkv) % 4 == 0:
         return kern, B * (Hq // 4) * -(-S // 64), 256

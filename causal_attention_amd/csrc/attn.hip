@@ -85,7 +85,7 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
                    int causal, void* stream, int use_rope = 0,
                    const attn::RopeRates& rope = attn::RopeRates{},
                    const int* cu_seqlens = nullptr,
-                   const int* seq_lens = nullptr) {
+                   const int* seq_lens = nullptr, void* split_ws = nullptr) {
   const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
   const dim3 grid((unsigned)(B * Hq * n_qtiles));
   const dim3 block(kPrefillThreads);
@@ -96,20 +96,20 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
                               sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens);
+                              cu_seqlens, seq_lens, split_ws);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens);
+                              cu_seqlens, seq_lens, split_ws);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens);
+                              cu_seqlens, seq_lens, split_ws);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                 S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens);
+                              cu_seqlens, seq_lens, split_ws);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -134,6 +134,37 @@ bool prefill_use_rb(int B, int Hq, int S, int D, int causal) {
   return work >= 4e8;
 }
 
+// Bound of the balanced schedule's wait for a partner's part, in ticks of
+// the 100 MHz real-time counter (-1: the kernel's own rule).
+std::atomic<int> g_split_wait{-1};
+
+// Pairs of the balanced causal schedule of the register-blocked kernel
+// (four query heads per workgroup), 0 where it does not apply: causal, head
+// dim 128, group size a multiple of 4, at least two 64-row query tiles, and
+// all of the launch's workgroups resident at once (one per compute unit),
+// where the unbalanced schedule lasts as long as its last query tile.  The
+// automatic choice takes it from S = 2048 on: measured on MI355X (causal,
+// bf16, 8/2 heads), 5% ahead of the 4-wave kernel at B = 4, S = 2048, level
+// at B = 1, S = 2048, 21-29% ahead at S = 4096 and 8192, and behind at
+// S <= 1024, where each workgroup's 17 or fewer key tiles do not repay the
+// second job's start and the hand-off.  ATTN_PREFILL_RB takes it wherever
+// it applies.
+constexpr int kSplitMinS = 2048;
+long long prefill_split_pairs(int B, int Hq, int Hkv, int S, int D,
+                              int causal) {
+  if (!causal || D != 128 || Hkv <= 0 || Hq % Hkv != 0 ||
+      (Hq / Hkv) % 4 != 0 || B <= 0 || S <= 0)
+    return 0;
+  const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
+  if (sel == ATTN_PREFILL_W4) return 0;
+  if (sel == ATTN_PREFILL_AUTO && S < kSplitMinS) return 0;
+  const long long nq = (S + 63) / 64;
+  if (nq < 2) return 0;
+  if ((long long)B * (Hq / 4) * nq > device_cu_count()) return 0;
+  const long long np = (long long)B * (Hq / 4) * (nq / 2);
+  return np <= attn::kRBMaxPairs ? np : 0;
+}
+
 // 16-bit inputs (bf16 or fp16): the MFMA kernels for element type T.
 template <typename T>
 struct Half16Prefill {
@@ -143,8 +174,21 @@ struct Half16Prefill {
                     const T* v, T* o, float* lse, int B, int Hq, int Hkv,
                     int S, float sl2, int nq, int ncu, int use_rope,
                     const attn::RopeRates& rope, const int* cu_seqlens,
-                    const int* seq_lens) {
+                    const int* seq_lens, void* split_ws) {
       if constexpr (D == 128) {
+        if constexpr (C) {
+          if (split_ws != nullptr) {
+            // balanced causal schedule, four query heads per workgroup
+            const int nq4 = (S + 63) / 64;
+            hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 4, true>),
+                               dim3((unsigned)(B * (Hq / 4) * nq4)),
+                               dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
+                               S, sl2, nq4, ncu, 0, rope, nullptr, nullptr,
+                               split_ws,
+                               g_split_wait.load(std::memory_order_relaxed));
+            return;
+          }
+        }
         if (prefill_use_rb(B, Hq, S, D, C)) {
           if ((Hq / Hkv) % 4 == 0) {
             // four query heads of a KV head per workgroup, 64-row tiles
@@ -153,12 +197,12 @@ struct Half16Prefill {
                                dim3((unsigned)(B * (Hq / 4) * nq4)),
                                dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq4, ncu, use_rope, rope, cu_seqlens,
-                               seq_lens);
+                               seq_lens, nullptr, -1);
           } else {
             hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 1>), g,
                                dim3(128), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq, ncu, use_rope, rope, cu_seqlens,
-                               seq_lens);
+                               seq_lens, nullptr, -1);
           }
           return;
         }
@@ -176,7 +220,8 @@ struct F32Prefill {
                   const float* k, const float* v, float* o, float* lse, int B,
                   int Hq, int Hkv, int S, float sl2, int nq, int ncu,
                   int /*use_rope*/, const attn::RopeRates& /*rope*/,
-                  const int* /*cu_seqlens*/, const int* /*seq_lens*/) {
+                  const int* /*cu_seqlens*/, const int* /*seq_lens*/,
+                  void* /*split_ws*/) {
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
                        k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }
@@ -265,18 +310,32 @@ void launch_decode_d(int G, const T* q, const T* kc, const T* vc,
 }
 
 // Shared body of the bf16 and fp16 prefill entry points.
+// A workspace (nullable) enables the balanced causal schedule where it
+// applies; it is ignored elsewhere.
 template <typename T>
 int prefill16(const void* q, const void* k, const void* v, void* o,
               float* lse, int B, int Hq, int Hkv, int S, int D, float scale,
-              int causal, void* stream) {
+              int causal, void* stream, void* workspace = nullptr,
+              size_t workspace_bytes = 0) {
   bool empty;
   const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
                                &empty);
   if (st != ATTN_OK || empty) return st;
+  void* split_ws = nullptr;
+  if (workspace != nullptr) {
+    const long long np = prefill_split_pairs(B, Hq, Hkv, S, D, causal);
+    if (np > 0) {
+      if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+      if (workspace_bytes < attn::rb_split_bytes(np))
+        return ATTN_ERR_WORKSPACE;
+      split_ws = workspace;
+    }
+  }
   return launch_prefill<T, Half16Prefill<T>::template L>(
       static_cast<const T*>(q), static_cast<const T*>(k),
       static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv, S, D,
-      scale, causal, stream);
+      scale, causal, stream, 0, attn::RopeRates{}, nullptr, nullptr,
+      split_ws);
 }
 
 // Shared body of the decode entry points; cap = 0 for the packed cache, else
@@ -487,6 +546,29 @@ int attn_prefill_f16(const void* q, const void* k, const void* v, void* o,
                              stream);
 }
 
+size_t attn_prefill_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                   int causal) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
+  const long long np = prefill_split_pairs(B, Hq, Hkv, S, D, causal);
+  return np > 0 ? attn::rb_split_bytes(np) : 0;
+}
+
+int attn_prefill_ws(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int Hq, int Hkv, int S, int D,
+                    float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return prefill16<__bf16>(q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal,
+                           stream, workspace, workspace_bytes);
+}
+
+int attn_prefill_ws_f16(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int B, int Hq, int Hkv, int S, int D,
+                        float scale, int causal, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return prefill16<_Float16>(q, k, v, o, lse, B, Hq, Hkv, S, D, scale,
+                             causal, stream, workspace, workspace_bytes);
+}
+
 int attn_prefill_rope(const void* q, const void* k, const void* v, void* o,
                       float* lse, void* k_rot, int B, int Hq, int Hkv, int S,
                       int D, float scale, int causal, float rope_base,
@@ -552,6 +634,11 @@ int attn_decode_auto_splits(int B, int Hkv) { return auto_splits(B, Hkv); }
 int attn_prefill_kernel_for(int B, int Hq, int S, int D, int causal) {
   return prefill_use_rb(B, Hq, S, D, causal) ? ATTN_PREFILL_RB
                                              : ATTN_PREFILL_W4;
+}
+
+int attn_prefill_split_wait(int ticks) {
+  if (ticks < -1) return ATTN_ERR_SHAPE;
+  return g_split_wait.exchange(ticks);
 }
 
 int attn_prefill_select(int kernel) {

@@ -666,22 +666,126 @@ __device__ __forceinline__ void mfma_to_valu_wait(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 15\n\ts_nop 2" : "+v"(s0), "+v"(s1));
 }
 
+// Balanced causal schedule of the four-heads form, for launches whose
+// 64-row query tiles all run at once (one workgroup per compute unit).
+// Query tile t needs n_t key tiles, growing with t, so with one tile per
+// compute unit the launch lasts as long as its last tile.  Instead tiles
+// l and nq-1-l are paired and their n_l + n_h key tiles are cut evenly
+// between two workgroups: A runs key tiles 0 .. c-1 of the heavy tile h,
+// c = (n_h - n_l) / 2, leaves that partial state (unnormalised O, reference
+// m, row sums l, lane by lane) in the workspace and then runs tile l whole;
+// B runs key tiles c .. n_h-1 of tile h and merges A's part into its own
+// before it writes tile h (two key ranges of one row merged with their
+// maxima and sums, as in section 4.4 of the attention-fusion page).  With
+// nq odd the middle tile runs alone: its key tiles equal half a pair's.
+//
+// Hand-off: flag word p of the workspace is 0 between launches.  A writes
+// its part, waits until the stores are acknowledged, then sets the flag
+// 0 -> 1.  B polls it for a bounded time; on time-out it sets 0 -> 2 and
+// runs tile h whole itself, and A, finding 2, puts back 0.  Both compare-
+// and-swaps hit the same word, so exactly one of the two orders happens,
+// and in each the flag ends 0: no workgroup ever waits without bound and
+// the next launch starts from zeros.  Part and flag travel with
+// device-coherent (agent-scope) accesses, which bypass the per-XCD L2s
+// (A and B may sit on different XCDs), instead of a release / acquire pair,
+// whose L2 write-back and invalidation cost several microseconds each.
+// Device-coherent 16-byte stores and loads (agent scope: past the per-XCD
+// L2, to the level all XCDs share), as assembly: the compiler has no
+// 16-byte atomic access.  The store ends with a wait state, so that its
+// data registers may be rewritten at once.
+__device__ __forceinline__ void coherent_store16(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1"
+               :
+               : "v"(p), "v"(v)
+               : "memory");
+}
+// Sixteen device-coherent 16-byte loads, chunk c (c = 0 .. 15) at
+// p + c * 1024 bytes, and the wait for all of them in one statement (no
+// result register is read or copied before its data has arrived); the
+// second form also loads chunk 16 from q.
+__device__ __forceinline__ void coherent_load16x16(f32x4 (&v)[16],
+                                                   const float* p) {
+  const char* b = reinterpret_cast<const char*>(p);
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off offset:0 sc1\n\tglobal_load_dwordx4 %1, %16, off offset:1024 sc1\n\tglobal_load_dwordx4 %2, %16, off offset:2048 sc1\n\tglobal_load_dwordx4 %3, %16, off offset:3072 sc1\n\tglobal_load_dwordx4 %4, %17, off offset:0 sc1\n\tglobal_load_dwordx4 %5, %17, off offset:1024 sc1\n\tglobal_load_dwordx4 %6, %17, off offset:2048 sc1\n\tglobal_load_dwordx4 %7, %17, off offset:3072 sc1\n\tglobal_load_dwordx4 %8, %18, off offset:0 sc1\n\tglobal_load_dwordx4 %9, %18, off offset:1024 sc1\n\tglobal_load_dwordx4 %10, %18, off offset:2048 sc1\n\tglobal_load_dwordx4 %11, %18, off offset:3072 sc1\n\tglobal_load_dwordx4 %12, %19, off offset:0 sc1\n\tglobal_load_dwordx4 %13, %19, off offset:1024 sc1\n\tglobal_load_dwordx4 %14, %19, off offset:2048 sc1\n\tglobal_load_dwordx4 %15, %19, off offset:3072 sc1\n\ts_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
+        "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]),
+        "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+        "=&v"(v[14]), "=&v"(v[15])
+      : "v"(b), "v"(b + 4096), "v"(b + 8192), "v"(b + 12288)
+      : "memory");
+}
+__device__ __forceinline__ void coherent_load16x17(f32x4 (&v)[17],
+                                                   const float* p,
+                                                   const float* q) {
+  const char* b = reinterpret_cast<const char*>(p);
+  asm volatile(
+      "global_load_dwordx4 %0, %17, off offset:0 sc1\n\tglobal_load_dwordx4 %1, %17, off offset:1024 sc1\n\tglobal_load_dwordx4 %2, %17, off offset:2048 sc1\n\tglobal_load_dwordx4 %3, %17, off offset:3072 sc1\n\tglobal_load_dwordx4 %4, %18, off offset:0 sc1\n\tglobal_load_dwordx4 %5, %18, off offset:1024 sc1\n\tglobal_load_dwordx4 %6, %18, off offset:2048 sc1\n\tglobal_load_dwordx4 %7, %18, off offset:3072 sc1\n\tglobal_load_dwordx4 %8, %19, off offset:0 sc1\n\tglobal_load_dwordx4 %9, %19, off offset:1024 sc1\n\tglobal_load_dwordx4 %10, %19, off offset:2048 sc1\n\tglobal_load_dwordx4 %11, %19, off offset:3072 sc1\n\tglobal_load_dwordx4 %12, %20, off offset:0 sc1\n\tglobal_load_dwordx4 %13, %20, off offset:1024 sc1\n\tglobal_load_dwordx4 %14, %20, off offset:2048 sc1\n\tglobal_load_dwordx4 %15, %20, off offset:3072 sc1\n\tglobal_load_dwordx4 %16, %21, off sc1\n\ts_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
+        "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]),
+        "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+        "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16])
+      : "v"(b), "v"(b + 4096), "v"(b + 8192), "v"(b + 12288), "v"(q)
+      : "memory");
+}
+
+struct SplitCoord {
+  int b, g, hgrp, pair, role;   // role 0: A, 1: B, 2: the middle tile alone
+};
+
+// Workgroups walk (batch, KV head) fastest, then head groups of that KV
+// head, then pair slots (A and B of a pair adjacent).
+__device__ __forceinline__ SplitCoord split_coord(int bid, int B, int Hgrp,
+                                                  int Hkv, int nq) {
+  const int P = B * Hkv;
+  const int bg = bid % P;
+  const int rest = bid / P;
+  const int Gg = Hgrp / Hkv;
+  SplitCoord c;
+  c.b = bg / Hkv;
+  c.g = bg % Hkv;
+  c.hgrp = c.g * Gg + rest % Gg;
+  const int slot = rest / Gg;
+  c.pair = slot >> 1;
+  c.role = ((nq & 1) && slot == nq - 1) ? 2 : (slot & 1);
+  return c;
+}
+
+// Causal key tiles (32 keys) of 64-row query tile t.
+__host__ __device__ __forceinline__ int rb_causal_tiles(int t, int S) {
+  const int hi = 64 * t + 64 < S ? 64 * t + 64 : S;
+  return (hi + 31) / 32;
+}
+
+// Workspace of the balanced schedule: a fixed region of flag words (one
+// per pair, at most kRBMaxPairs; the same place for every launch, so one
+// workspace serves launches of any sizes), then per pair, wave and 16-byte
+// chunk (32 of O, one of m and l) the 64 lanes' values.
+constexpr int kRBDumpChunks = 33;
+constexpr int kRBFlagBytes = 4096;
+constexpr int kRBMaxPairs = kRBFlagBytes / 4;
+__host__ __device__ __forceinline__ size_t rb_split_bytes(long long np) {
+  return (size_t)kRBFlagBytes + (size_t)np * 4 * kRBDumpChunks * 64 * 16;
+}
+
 // GQ = 1: one query head per workgroup, 2 waves x 64 rows (128-row query
 // tiles, two workgroups per compute unit).  GQ = 4: four query heads of one
 // KV head per workgroup, one wave per head on the same 64 rows (64-row
 // query tiles, one workgroup per compute unit): every K / V tile loaded
 // into LDS feeds 256 query rows instead of 128, and all waves share one
 // causal diagonal.
-template <typename T, int D, bool CAUSAL, int GQ>
+template <typename T, int D, bool CAUSAL, int GQ, bool SPLIT = false>
 __global__ __launch_bounds__(GQ == 4 ? 256 : 128, GQ == 4 ? 1 : 2)
 void attn_prefill_rb_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
     float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
-    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
+    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens,
+    void* __restrict__ ws, int wait_ticks) {
   static_assert(D == 128, "64 rows per wave at head dim 128");
   static_assert(GQ == 1 || GQ == 4, "heads per workgroup");
+  static_assert(!SPLIT || (GQ == 4 && CAUSAL), "balanced causal schedule");
   constexpr int WAVES = GQ == 4 ? 4 : 2;
   constexpr int BM = GQ == 4 ? 64 : 128;      // query rows per head
   constexpr int TK = 32;                      // keys per tile
@@ -702,9 +806,26 @@ void attn_prefill_rb_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  // (batch, KV head, head group, query tile); this wave's query head
-  const TileCoord tc =
-      tile_coord(blockIdx.x, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, n_cu);
+  // (batch, KV head, head group, query tile); this wave's query head.  The
+  // balanced schedule (SPLIT) takes dense inputs without RoPE.
+  const unsigned long long t_start =
+      SPLIT ? __builtin_amdgcn_s_memrealtime() : 0ull;
+  if constexpr (SPLIT) {
+    use_rope = 0;
+    cu_seqlens = nullptr;
+    seq_lens = nullptr;
+  }
+  TileCoord tc;
+  SplitCoord sc{};
+  if constexpr (SPLIT) {
+    sc = split_coord(blockIdx.x, B, Hq / GQ, Hkv, n_qtiles);
+    tc.b = sc.b;
+    tc.g = sc.g;
+    tc.hq = sc.hgrp;
+    tc.qt = sc.pair;
+  } else {
+    tc = tile_coord(blockIdx.x, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, n_cu);
+  }
   const int hq = tc.hq * GQ + (GQ == 4 ? w : 0);
 
   int S = S_all;
@@ -727,46 +848,71 @@ void attn_prefill_rb_kernel(
       *reinterpret_cast<u32x4*>(orow + 8 * c) = u32x4{};
     if (LSE != nullptr && hh == 0) LSE[q_row0 + row] = -INFINITY;
   };
-  const int q_lo = tc.qt * BM;
-  const int wq0 = q_lo + (GQ == 4 ? 0 : 64 * w);   // first row of this wave
-  if (seq_lens != nullptr && q_lo >= S) {
+  if (seq_lens != nullptr && tc.qt * BM >= S) {
+    const int wq = tc.qt * BM + (GQ == 4 ? 0 : 64 * w);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
-      if (wq0 + 32 * rb + r < S_all) pad_row(wq0 + 32 * rb + r);
+      if (wq + 32 * rb + r < S_all) pad_row(wq + 32 * rb + r);
     return;
   }
   const T* Qp = Q + q_row0 * D;
-  const int q_hi = min(S, q_lo + BM);
-  const int kv_end = CAUSAL ? q_hi : S;
-  const int n = (kv_end + TK - 1) / TK;       // key tiles (>= 1)
-  const int n_full = min(min(n, S / TK), CAUSAL ? (q_lo + 1) / TK : n);
 
-  // Q^T B operands of both row blocks (AGPRs, through the QK^T assembly).
-  u32x4 qB[2][KT];
+  // The current job: query tile q_lo / BM against key tiles
+  // kbase / TK .. kbase / TK + n - 1 (all tiles counted from kbase on).
+  int q_lo = 0, wq0 = 0;      // first row of the tile, of this wave
+  int kbase = 0, n = 0;       // first key, key tiles (>= 1)
+  int n_full = 0;             // leading tiles that need no mask
+  int n_plain = 0;            // ... whose loads five tiles on are full
+  int s_rel = 0, jmax = 0;    // keys from kbase on, last tile holding keys
+  u32x4 krs, vrs;             // K, V from row kbase of this KV head
+  u32x4 qB[2][KT];            // Q^T B operands of both row blocks (AGPRs)
+  auto setup_job = [&](int qt, int jlo, int jhi) {
+    q_lo = qt * BM;
+    wq0 = q_lo + (GQ == 4 ? 0 : 64 * w);
+    const int q_hi = min(S, q_lo + BM);
+    const int n_abs = ((CAUSAL ? q_hi : S) + TK - 1) / TK;
+    kbase = jlo * TK;
+    n = min(jhi, n_abs) - jlo;
+    s_rel = S - kbase;
+    const int s_tiles = s_rel / TK;
+    n_full = max(0, min(min(n, s_tiles), CAUSAL ? (q_lo + 1) / TK - jlo : n));
+    n_plain = min(n_full, s_tiles - 5);
+    jmax = (s_rel - 1) / TK;
+    krs = buffer_rsrc(K + (kv_row0 + kbase) * D);
+    vrs = buffer_rsrc(V + (kv_row0 + kbase) * D);
+  };
+  // Q^T operands of the job's rows, loaded before the job's first K / V
+  // loads.  Loaded later, inside the pass, the compiler no longer keeps
+  // them in their own AGPRs for the whole job but copies each into a
+  // shared one right after the (assembly) MFMA that read the previous one.
+  auto load_q = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int query = wq0 + 32 * rb + r;
-    x8 qv[KT];
+    for (int rb = 0; rb < 2; ++rb) {
+      const int query = wq0 + 32 * rb + r;
+      x8 qv[KT];
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-      qv[t] = query < S ? *reinterpret_cast<const x8*>(
-                              Qp + (size_t)query * D + 16 * t + 8 * hh)
-                        : x8{};
-    if (use_rope) {
+      for (int t = 0; t < KT; ++t)
+        qv[t] = query < S ? *reinterpret_cast<const x8*>(
+                                Qp + (size_t)query * D + 16 * t + 8 * hh)
+                          : x8{};
+      if (use_rope) {
 #pragma unroll
-      for (int t = 0; t < KT / 2; ++t)
+        for (int t = 0; t < KT / 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x1 = (float)qv[t][e], x2 = (float)qv[t + KT / 2][e];
-          const double rr = hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
-          rope_pair(x1, x2, query, rr);
-          qv[t][e] = (T)x1;
-          qv[t + KT / 2][e] = (T)x2;
-        }
+          for (int e = 0; e < 8; ++e) {
+            float x1 = (float)qv[t][e], x2 = (float)qv[t + KT / 2][e];
+            const double rr =
+                hh ? rope.r[16 * t + 8 + e] : rope.r[16 * t + e];
+            rope_pair(x1, x2, query, rr);
+            qv[t][e] = (T)x1;
+            qv[t + KT / 2][e] = (T)x2;
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        qB[rb][t] = __builtin_bit_cast(u32x4, qv[t]);
     }
-#pragma unroll
-    for (int t = 0; t < KT; ++t) qB[rb][t] = __builtin_bit_cast(u32x4, qv[t]);
-  }
+  };
 
   // Direct loads: wave w fills 1 KB blocks IPW w .. IPW w + IPW-1 of a tile.
   unsigned koffr[IPW], voffr[IPW];
@@ -776,13 +922,10 @@ void attn_prefill_rb_kernel(
     koffr[ii] = (row * D + 8 * swz_k<CPR>(row, pos)) * 2 - ii * 1024;
     voffr[ii] = (row * D + 8 * swz_v<CPR>(row, pos)) * 2 - ii * 1024;
   }
-  const u32x4 krs = buffer_rsrc(K + kv_row0 * D);
-  const u32x4 vrs = buffer_rsrc(V + kv_row0 * D);
-  // Load II of this wave's share of K (kv = 0) or V (kv = 1) tile j into
-  // ring slot j % NB.  A tile past the last one holding keys loads that one
-  // instead (its slot is not read again); rows past S load row S - 1 (their
-  // scores are masked).
-  const int jmax = (S - 1) / TK;
+  // Load II of this wave's share of K (kv = 0) or V (kv = 1) tile j of the
+  // job (key tile kbase / TK + j) into ring slot j % NB.  A tile past the
+  // last one holding keys loads that one instead (its slot is not read
+  // again); rows past S load row S - 1 (their scores are masked).
   auto issue1 = [&](int kv, int j, auto ii_c, auto full_c) {
     constexpr int II = decltype(ii_c)::value;
     if constexpr (decltype(full_c)::value) {   // tile j known full
@@ -796,11 +939,11 @@ void attn_prefill_rb_kernel(
     unsigned char* dst = smem + (j % NB) * SLOT + kv * TILE + w * IPW * 1024;
     const u32x4& rs = kv ? vrs : krs;
     const unsigned voff = kv ? voffr[II] : koffr[II];
-    if (j0 + TK <= S) {
+    if (j0 + TK <= s_rel) {
       lds_buffer_load16_at<II>(rs, voff, soff, dst);
     } else {
       const int row = (w * IPW + II) * RPI + lane / CPR;
-      const int back = (min(j0 + row, S - 1) - (j0 + row)) * D * 2;
+      const int back = (min(j0 + row, s_rel - 1) - (j0 + row)) * D * 2;
       lds_buffer_load16(rs, voff + II * 1024 + back, soff, dst + II * 1024);
     }
   };
@@ -850,8 +993,8 @@ void attn_prefill_rb_kernel(
   // for key tile i.
   auto mask4 = [&](auto buf_c, int rb, int e0, int i) {
     constexpr int SB = decltype(buf_c)::value;
-    apply_mask_lim4<CAUSAL>(sbuf[SB][rb], e0, i * TK, hh, wq0 + 32 * rb + r,
-                            S);
+    apply_mask_lim4<CAUSAL>(sbuf[SB][rb], e0, kbase + i * TK, hh,
+                            wq0 + 32 * rb + r, S);
   };
   // Row max (log2 domain) of one row block of buffer SB.
   auto rowmax = [&](auto buf_c, int rb) {
@@ -1057,7 +1200,6 @@ void attn_prefill_rb_kernel(
     using Masked = std::true_type;
     using Full = std::true_type;
     using Any = std::false_type;
-    const int n_plain = min(n_full, S / TK - 5);   // it + 8 < S / TK
     int it = 0;
     for (; it + 4 < n_plain; it += 4) {
       tile(C0{}, Plain{}, Full{}, it);
@@ -1080,28 +1222,198 @@ void attn_prefill_rb_kernel(
   // bounds every score of the row from above (l >= each p), so that p <= 1;
   // after an fp32 overflow (some p >= 2^128 / S), m + 100 is still below the
   // row's max.  Rows within the headroom take the new m as well.
-  float m_next[2] = {0.f, 0.f};
   constexpr float kLimit = (float)(1ull << (int)rb_headroom<T>());
-  for (int pass = 0; pass < kRBMaxPasses; ++pass) {
-    run_pass(pass, m_next);
-    bool over = false;
+  // The job's passes; at the end every load has landed and every LDS read
+  // is done (the loop's last barrier).
+  auto run_job = [&]() {
+    float m_next[2] = {0.f, 0.f};
+    for (int pass = 0; pass < kRBMaxPasses; ++pass) {
+      run_pass(pass, m_next);
+      bool over = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float l_tot = l_i[rb] + swap_halves(l_i[rb]);
-      const bool inf = l_tot == INFINITY;
-      over = over || inf || l_tot > kLimit;
-      m_next[rb] = m_ref[rb] + (inf ? 100.f : fast_log2(l_tot));
+      for (int rb = 0; rb < 2; ++rb) {
+        const float l_tot = l_i[rb] + swap_halves(l_i[rb]);
+        const bool inf = l_tot == INFINITY;
+        over = over || inf || l_tot > kLimit;
+        m_next[rb] = m_ref[rb] + (inf ? 100.f : fast_log2(l_tot));
+      }
+      int* flag = reinterpret_cast<int*>(smem);
+      const int any = __ballot(over) != 0;    // with every lane active
+      if (lane == 0) flag[w] = any;
+      __syncthreads();
+      int any_w = 0;
+#pragma unroll
+      for (int x = 0; x < WAVES; ++x) any_w |= flag[x];
+      const bool again = any_w != 0;
+      __syncthreads();
+      if (!again) break;
     }
-    int* flag = reinterpret_cast<int*>(smem);
-    const int any = __ballot(over) != 0;      // with every lane active
-    if (lane == 0) flag[w] = any;
-    __syncthreads();
-    int any_w = 0;
+  };
+
+  // Jobs: the whole tile, or under the balanced schedule A's part of the
+  // heavy tile (kept in the workspace) and then the light tile, B's part of
+  // the heavy tile merged with A's, or the middle tile.
+  enum { kFinal = 0, kPart = 1, kMerge = 2 };
+  int jq = tc.qt, jlo = 0, jhi = 1 << 30, jmode = kFinal;
+  // pair index, heavy tile, flag words and this lane's part of the pair
+  // (the SPLIT instantiation only; ws is non-null there)
+  const int np_bg = n_qtiles / 2;       // pairs per (batch, head group)
+  const int pidx = (sc.b * (Hq / GQ) + sc.hgrp) * np_bg + sc.pair;
+  const int qt_h = n_qtiles - 1 - sc.pair;
+  int* const flags = static_cast<int*>(ws);
+  // wave-uniform base (scalar registers); value q of chunk c of lane l at
+  // (c * 64 + l) * 4 + q
+  float* const dump = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                               kRBFlagBytes) +
+                      ((size_t)pidx * WAVES + w) * (kRBDumpChunks * 64 * 4);
+  if constexpr (SPLIT) {
+    {
+      const int c = sc.role == 2 ? 0
+                                 : (rb_causal_tiles(qt_h, S) -
+                                    rb_causal_tiles(sc.pair, S)) / 2;
+      if (sc.role == 0 && c > 0) {
+        jq = qt_h;
+        jhi = c;
+        jmode = kPart;
+      } else if (sc.role == 1) {
+        jq = qt_h;
+        jlo = c;
+        jmode = c > 0 ? kMerge : kFinal;
+      }
+    }
+  }
+
+  while (true) {
+    setup_job(jq, jlo, jhi);
+    load_q();
+    run_job();
+    if constexpr (SPLIT) {
+      if (jmode == kPart) {
+        // A: the part, then flag 0 -> 1 (or 2 -> 0 when B gave up on it).
+        // Part and flag are written with device-coherent (agent-scope)
+        // accesses, which go past this XCD's L2 to memory, so no cache
+        // write-back is needed: every wave waits for its stores to be
+        // acknowledged before the barrier, and only then is the flag set.
+        // The lane index passes through an empty statement so that the
+        // addresses are formed here, not hoisted out of the job loop (33 of
+        // them would not fit in registers).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int x = 0; x < WAVES; ++x) any_w |= flag[x];
-    const bool again = any_w != 0;
-    __syncthreads();
-    if (!again) break;
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              coherent_store16(
+                  dump + (((rb * NDB + db) * 4 + a) * 64 + ln) * 4,
+                  f32x4{oacc[rb][db][4 * a], oacc[rb][db][4 * a + 1],
+                        oacc[rb][db][4 * a + 2], oacc[rb][db][4 * a + 3]});
+        coherent_store16(dump + (32 * 64 + ln) * 4,
+                         f32x4{m_ref[0], m_ref[1], l_i[0], l_i[1]});
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+          int expected = 0;
+          if (!__hip_atomic_compare_exchange_strong(
+                  flags + pidx, &expected, 1, __ATOMIC_RELAXED,
+                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            __hip_atomic_store(flags + pidx, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        jq = sc.pair;
+        jlo = 0;
+        jhi = 1 << 30;
+        jmode = kFinal;
+        continue;
+      }
+      if (jmode == kMerge) {
+        // B: wait for A's part, at most twice as long as this workgroup
+        // has run so far plus 20 us, or wait_ticks if >= 0 (real-time
+        // counter, 100 MHz)
+        int* got_s = reinterpret_cast<int*>(smem) + 8;
+        if (tid == 0) {
+          const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+          const unsigned long long deadline =
+              now + (wait_ticks >= 0 ? (unsigned long long)wait_ticks
+                                     : 2 * (now - t_start) + 2000);
+          int got = 0;
+          while (true) {
+            // device-coherent polls (an acquire would also invalidate the
+            // L2 each time)
+            if (__hip_atomic_load(flags + pidx, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == 1) {
+              got = 1;
+              break;
+            }
+            if (__builtin_amdgcn_s_memrealtime() > deadline) {
+              int expected = 0;
+              got = __hip_atomic_compare_exchange_strong(
+                        flags + pidx, &expected, 2, __ATOMIC_RELAXED,
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        ? 0
+                        : 1;           // A posted meanwhile
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          if (got)
+            __hip_atomic_store(flags + pidx, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          *got_s = got;
+        }
+        __syncthreads();
+        const int got = __builtin_amdgcn_readfirstlane(*got_s);
+        __syncthreads();
+        if (!got) {                    // run the heavy tile whole
+          jlo = 0;
+          jmode = kFinal;
+          continue;
+        }
+        // the part is read with device-coherent loads, issued after the
+        // flag was seen (the barrier above), so they see A's stores
+        // the part in two batches of loads in flight together: m and l
+        // with O chunks 0 .. 15, then chunks 16 .. 31 (addresses formed
+        // here, as for the stores)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        float fa[2], fb[2];
+        {
+          f32x4 part[17];
+          coherent_load16x17(part, dump + ln * 4, dump + (32 * 64 + ln) * 4);
+          const f32x4 ml = part[16];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float mx = fmaxf(ml[rb], m_ref[rb]);
+            fa[rb] = fast_exp2(ml[rb] - mx);
+            fb[rb] = fast_exp2(m_ref[rb] - mx);
+            l_i[rb] = fa[rb] * ml[2 + rb] + fb[rb] * l_i[rb];
+            m_ref[rb] = mx;
+          }
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const int rb = c >> 4, db = (c >> 2) & 3, a = c & 3;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              oacc[rb][db][4 * a + q] =
+                  fa[rb] * part[c][q] + fb[rb] * oacc[rb][db][4 * a + q];
+          }
+        }
+        {
+          f32x4 part[16];
+          coherent_load16x16(part, dump + (16 * 64 + ln) * 4);
+#pragma unroll
+          for (int c = 16; c < 32; ++c) {
+            const int rb = c >> 4, db = (c >> 2) & 3, a = c & 3;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              oacc[rb][db][4 * a + q] = fa[rb] * part[c - 16][q] +
+                                        fb[rb] * oacc[rb][db][4 * a + q];
+          }
+        }
+      }
+    }
+    break;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m_ref + log2 l) ln 2

@@ -45,7 +45,7 @@ typedef enum {
                               unsupported group size Hq / Hkv */
   ATTN_ERR_HEAD_DIM = -4,  /* D is not 64 or 128 */
   ATTN_ERR_ALIGN = -5,     /* a pointer is not aligned as required */
-  ATTN_ERR_WORKSPACE = -6, /* decode workspace smaller than required */
+  ATTN_ERR_WORKSPACE = -6, /* workspace smaller than required */
   ATTN_ERR_SPLITS = -7,    /* num_splits < 0 or > ATTN_MAX_SPLITS */
   ATTN_ERR_LAUNCH = -8,    /* the HIP runtime rejected a kernel launch */
   ATTN_ERR_SCALE = -9      /* scale is not a finite positive number (or a
@@ -74,6 +74,48 @@ typedef enum {
 int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  float* lse, int B, int Hq, int Hkv, int S, int D,
                  float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace that let attn_prefill_ws (and _ws_f16) run a
+ * causal launch with the balanced schedule, 0 where that schedule does not
+ * apply.  It applies to causal launches with D = 128, Hq / Hkv a multiple
+ * of 4, S > 64, and at most one workgroup of B (Hq/4) ceil(S/64) per
+ * compute unit of the current device; under ATTN_PREFILL_AUTO from
+ * S = 2048 on (below that the 4-wave kernel was measured faster), under
+ * ATTN_PREFILL_RB for any such S, under ATTN_PREFILL_W4 never.
+ * Query tile t needs a number of key tiles growing with t, so when every
+ * tile has its own compute unit the launch otherwise lasts as long as its
+ * last tile; the balanced schedule pairs tile t with tile nq-1-t and cuts
+ * the pair's key tiles evenly between two workgroups, the second merging
+ * the first's part of the longer row range with its own (the merge of key
+ * ranges by their maxima and sums, attention-fusion page, section 4.4, with
+ * the partial buffer of the Qwen page, section 3.3).  The size depends on
+ * the device's compute-unit count: query it with that device current.
+ */
+size_t attn_prefill_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                   int causal);
+
+/*
+ * attn_prefill / attn_prefill_f16 with a caller-owned device workspace
+ * (16-byte aligned) for the balanced schedule.  workspace NULL, or a launch
+ * the schedule does not apply to: the same launch as attn_prefill.  Where
+ * it applies, workspace_bytes below attn_prefill_workspace_size is
+ * ATTN_ERR_WORKSPACE.  Its first 4096 bytes hold one flag word per pair of
+ * query tiles: they must be zero before the workspace's first use, and
+ * every call leaves them zero, so one workspace serves calls of any sizes
+ * in turn (the rest of the workspace may hold anything).  Calls that share
+ * a workspace must not overlap in time (launch them on one stream).  A workgroup waits for its partner's part
+ * for a bounded time only, then computes the part itself, so a launch
+ * always completes.  Other arguments and errors as attn_prefill.
+ */
+int attn_prefill_ws(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int Hq, int Hkv, int S, int D,
+                    float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int attn_prefill_ws_f16(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int B, int Hq, int Hkv, int S, int D,
+                        float scale, int causal, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * Prefill attention, fp16 storage.  Same arguments and layouts as
@@ -203,11 +245,24 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
 int attn_prefill_select(int kernel);
 
 /* The kernel (ATTN_PREFILL_W4 or ATTN_PREFILL_RB) a 16-bit prefill launch
-   with these sizes would use under the current setting.  W4 launches
+   with these sizes would use under the current setting, without a
+   workspace (with one, the balanced schedule runs the RB kernel, four heads
+   per workgroup, wherever attn_prefill_workspace_size is nonzero).  W4 launches
    B Hq ceil(S/128) workgroups of 256 threads; RB launches B (Hq/4)
    ceil(S/64) workgroups of 256 threads when Hq/Hkv is a multiple of 4,
    else B Hq ceil(S/128) of 128 threads. */
 int attn_prefill_kernel_for(int B, int Hq, int S, int D, int causal);
+
+/*
+ * How long, in ticks of the GPU's 100 MHz real-time counter, a workgroup of
+ * the balanced schedule waits for its partner's part before computing that
+ * part itself: -1 (the default) waits twice as long as the workgroup has
+ * run so far plus 20 us; 0 gives up at once.  Process-wide, for testing the
+ * give-up path and for tuning; the results are the same either way up to
+ * rounding order.  Returns the previous setting, or ATTN_ERR_SHAPE for a
+ * value below -1 (the setting is then unchanged).
+ */
+int attn_prefill_split_wait(int ticks);
 
 /*
  * Bytes of device workspace attn_decode needs for these sizes

@@ -32,6 +32,8 @@ def test_header_declares_the_entry_points():
               "attn_decode_padded_f16", "attn_decode_noalloc",
               "attn_decode_workspace_size", "attn_decode_auto_splits",
               "attn_prefill_select", "attn_prefill_kernel_for",
+              "attn_prefill_ws", "attn_prefill_ws_f16",
+              "attn_prefill_workspace_size", "attn_prefill_split_wait",
               "attn_status_string"]:
         assert n in names
 
@@ -73,6 +75,23 @@ def test_prefill_kernel_selection():
         attn.prefill_select(W4)
         assert attn.prefill_workgroups(2, 8, 2, 1000, 128) == (W4, 2 * 8 * 8,
                                                               256)
+        # with a workspace, causal four-heads launches of one round run the
+        # balanced schedule on the register-blocked kernel, whatever the
+        # table says (not under W4)
+        prev_ws = attn.prefill_workspace_policy(True)
+        try:
+            assert not attn.prefill_balanced(4, 8, 2, 2048, 128)
+            attn.prefill_select(attn.PREFILL_AUTO)
+            assert attn.prefill_balanced(4, 8, 2, 2048, 128)
+            assert attn.prefill_workgroups(4, 8, 2, 2048, 128) == (
+                RB, 4 * 2 * 32, 256)
+            assert not attn.prefill_balanced(4, 8, 2, 2048, 128,
+                                             causal=False)
+            attn.prefill_workspace_policy(False)
+            assert attn.prefill_workgroups(4, 8, 2, 2048, 128) == (
+                W4, 4 * 8 * 16, 256)
+        finally:
+            attn.prefill_workspace_policy(prev_ws)
         with pytest.raises(ValueError):
             attn.prefill_select(3)
     finally:
@@ -119,6 +138,67 @@ def test_prefill_empty_is_a_noop(fn):
     # B == 0 or S == 0: nothing to do, even with NULL pointers
     assert prefill(fn, q=None, k=None, v=None, o=None, lse=None, B=0) == 0
     assert prefill(fn, q=None, k=None, v=None, o=None, lse=None, S=0) == 0
+
+
+def test_prefill_workspace_size():
+    # host-only; without a GPU the library assumes 256 compute units
+    prev = attn.prefill_select(attn.PREFILL_AUTO)
+    try:
+        ws = attn.attn_prefill_workspace_size
+        # C3: 4 x 2 head groups x 32 query tiles = 256 workgroups, 128 pairs:
+        # a fixed 4 KB of flag words, then per pair 4 waves x 33 chunks x 64
+        # lanes x 16 B
+        assert ws(4, 8, 2, 2048, 128) == 4096 + 128 * 4 * 33 * 64 * 16
+        # automatic choice: from S = 2048 on only
+        assert ws(2, 8, 2, 300, 128) == 0
+        assert ws(1, 8, 2, 2047, 128) == 0
+        assert ws(1, 8, 2, 2048, 128) == 4096 + 32 * 4 * 33 * 64 * 16
+        assert ws(4, 8, 2, 2048, 128, causal=False) == 0
+        assert ws(4, 8, 2, 2048, 64) == 0          # head dim 64
+        assert ws(4, 8, 4, 2048, 128) == 0         # group size 2
+        assert ws(1, 8, 2, 64, 128) == 0           # one query tile
+        assert ws(8, 8, 2, 2048, 128) == 0         # two rounds of workgroups
+        assert ws(0, 8, 2, 2048, 128) == 0
+        # forced register-blocked kernel: wherever it applies; odd tile
+        # count: the middle tile has no pair
+        attn.prefill_select(attn.PREFILL_RB)
+        assert ws(2, 8, 2, 300, 128) == 4096 + 2 * 2 * 2 * 4 * 33 * 64 * 16
+        assert ws(1, 8, 2, 64, 128) == 0           # still one query tile
+        attn.prefill_select(attn.PREFILL_W4)
+        assert ws(4, 8, 2, 2048, 128) == 0
+    finally:
+        attn.prefill_select(prev)
+
+
+def test_prefill_split_wait_setting():
+    assert attn.lib().attn_prefill_split_wait(-2) == -2   # rejected
+    prev = attn.prefill_split_wait(0)
+    try:
+        assert prev == -1                                 # the default
+        assert attn.prefill_split_wait(500) == 0
+        with pytest.raises(ValueError):
+            attn.prefill_split_wait(-5)
+    finally:
+        attn.prefill_split_wait(prev)
+
+
+@pytest.mark.parametrize("fn", ["attn_prefill_ws", "attn_prefill_ws_f16"])
+def test_prefill_ws_argument_errors(fn):
+    L = attn.lib()
+    need = attn.attn_prefill_workspace_size(4, 8, 2, 2048, 128)
+
+    def call(ws=A, wsb=need, **kw):
+        a = dict(q=A, k=A, v=A, o=A, lse=A, B=4, Hq=8, Hkv=2, S=2048, D=128,
+                 scale=0.1, causal=1)
+        a.update(kw)
+        return getattr(L, fn)(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                              a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                              a["scale"], a["causal"], ws, wsb, None)
+    assert call(wsb=need - 1) == -6             # too small
+    assert call(ws=A + 8) == -5                 # not 16-byte aligned
+    assert call(q=None) == -1                   # prefill checks come first
+    assert call(Hq=8, Hkv=3) == -3
+    assert call(B=0, ws=None, wsb=0) == 0       # empty: no-op
 
 
 def decode(q=A, kc=A, vc=A, sl=A, o=A, B=4, Hq=8, Hkv=2, D=128, scale=0.1,

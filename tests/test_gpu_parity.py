@@ -640,6 +640,120 @@ def test_prefill_padded_matches_oracle(B, Hq, Hkv, S, D, lens, causal):
             assert eo <= o_tol("bf16") and el <= LSE_TOL
 
 
+def dense_one_range(q, k, v):
+    """Dense prefill without a workspace: every query tile in one workgroup
+    over its whole key range, the launch shape the padded and ragged entry
+    points share (the balanced schedule merges two key ranges of some tiles
+    and so rounds differently)."""
+    prev = attn.prefill_workspace_policy(False)
+    try:
+        return attn.attn_prefill(q, k, v)
+    finally:
+        attn.prefill_workspace_policy(prev)
+
+
+# ------------------------------------------- balanced causal schedule
+
+FLAG_BYTES = 4096      # the workspace's flag words, one per pair of tiles
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(4, 8, 2, 2048), (2, 8, 2, 300),
+                                        (1, 16, 4, 1000), (3, 8, 1, 129)])
+@pytest.mark.parametrize("wait", [-1, 0])
+def test_prefill_balanced_matches_oracle_and_leaves_flags_zero(B, Hq, Hkv, S,
+                                                               wait):
+    """The balanced schedule (forced on with the register-blocked kernel,
+    so that it also runs at sizes the automatic choice leaves to the 4-wave
+    kernel) against the oracle, with the hand-off waiting
+    by the kernel's rule (-1) or giving up at once (0: the second workgroup
+    of a pair computes the first one's part itself whenever the part is not
+    there yet).  The flag words are zero afterwards either way, and what the
+    rest of the workspace held does not matter."""
+    D = 128
+    say(f"[prefill balanced] B={B} Hq={Hq} Hkv={Hkv} S={S} wait={wait}")
+    prev_sel = attn.prefill_select(attn.PREFILL_RB)
+    prev_wait = attn.prefill_split_wait(wait)
+    try:
+        assert attn.attn_prefill_workspace_size(B, Hq, Hkv, S, D) > 0
+        q, k, v = (t.to(DEV) for t in
+                   inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 31))
+        ws = attn.new_prefill_workspace(B, Hq, Hkv, S, D, device=DEV)
+        nf = FLAG_BYTES
+        ws[nf:] = 0xFF                 # every float of the parts reads NaN
+        for rep in range(2):
+            o, lse = attn.attn_prefill(q, k, v, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:nf].count_nonzero()) == 0
+            if B * Hq * S <= 16 * 2048:
+                ro, rl = oracle.prefill(np64(q), np64(k), np64(v),
+                                        1 / math.sqrt(D), True)
+                eo = np.abs(np64(o) - ro).max()
+                el = np.abs(lse.cpu().numpy() - rl).max()
+            else:
+                rows = inputs.sampled_rows(Hq, S, 64)
+                ro, rl = oracle.prefill_rows(np64(q), np64(k), np64(v),
+                                             1 / math.sqrt(D), True, rows)
+                oo, ll = np64(o), lse.cpu().numpy()
+                eo = max(np.abs(oo[b][h][rows[h]] - ro[b, h]).max()
+                         for b in range(B) for h in range(Hq))
+                el = max(np.abs(ll[b][h][rows[h]] - rl[b, h]).max()
+                         for b in range(B) for h in range(Hq))
+            say(f"   rep {rep}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+            assert eo <= o_tol("bf16") and el <= LSE_TOL
+    finally:
+        attn.prefill_split_wait(prev_wait)
+        attn.prefill_select(prev_sel)
+
+
+def test_prefill_balanced_workspace_reused_across_sizes():
+    """One workspace serves launches of different sizes in turn (the flag
+    words sit in the same place for all): each launch (balanced schedule
+    forced on) matches the oracle on sampled rows and leaves the flags
+    zero."""
+    D = 128
+    prev_sel = attn.prefill_select(attn.PREFILL_RB)
+    try:
+        ws = attn.new_prefill_workspace(4, 8, 2, 2048, D, device=DEV)
+        for (B, Hq, Hkv, S) in [(4, 8, 2, 2048), (1, 8, 2, 4096),
+                                (2, 8, 2, 300), (4, 8, 2, 2048)]:
+            say(f"[prefill balanced reuse] B={B} Hq={Hq} Hkv={Hkv} S={S}")
+            assert 0 < attn.attn_prefill_workspace_size(B, Hq, Hkv, S,
+                                                        D) <= ws.numel()
+            q, k, v = (t.to(DEV) for t in
+                       inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0,
+                                             S))
+            o, lse = attn.attn_prefill(q, k, v, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:FLAG_BYTES].count_nonzero()) == 0
+            rows = inputs.sampled_rows(Hq, S, min(S, 64))
+            ro, rl = oracle.prefill_rows(np64(q), np64(k), np64(v),
+                                         1 / math.sqrt(D), True, rows)
+            oo, ll = np64(o), lse.cpu().numpy()
+            eo = max(np.abs(oo[b][h][rows[h]] - ro[b, h]).max()
+                     for b in range(B) for h in range(Hq))
+            el = max(np.abs(ll[b][h][rows[h]] - rl[b, h]).max()
+                     for b in range(B) for h in range(Hq))
+            say(f"   max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+            assert eo <= o_tol("bf16") and el <= LSE_TOL
+    finally:
+        attn.prefill_select(prev_sel)
+
+
+def test_prefill_balanced_is_the_default_and_reproducible():
+    """attn_prefill passes its own workspace: a C3-sized causal launch runs
+    the balanced schedule, and repeated calls (merging the same parts in
+    the same order) agree bit for bit."""
+    B, Hq, Hkv, S, D = 4, 8, 2, 2048, 128
+    say(f"[prefill balanced default] B={B} Hq={Hq} Hkv={Hkv} S={S}")
+    assert attn.prefill_balanced(B, Hq, Hkv, S, D)
+    q, k, v = (t.to(DEV) for t in
+               inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 32))
+    o1, l1 = attn.attn_prefill(q, k, v)
+    o2, l2 = attn.attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 @pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_padded_full_lengths_equal_dense_and_ignore_padding():
     # lengths = S: the dense kernel's results bit for bit; and values written
@@ -650,7 +764,7 @@ def test_prefill_padded_full_lengths_equal_dense_and_ignore_padding():
                inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 8))
     full = torch.full((B,), S, dtype=torch.int32, device=DEV)
     o1, l1 = attn.attn_prefill_padded(q, k, v, full)
-    o2, l2 = attn.attn_prefill(q, k, v)
+    o2, l2 = dense_one_range(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     lens = torch.tensor([77, 300], dtype=torch.int32, device=DEV)
@@ -776,7 +890,7 @@ def test_prefill_varlen_equal_lengths_is_the_dense_kernel():
                                                          "bf16", 1.0, 3))
     cu = torch.arange(B + 1, dtype=torch.int32, device=DEV) * S
     o, lse = attn.attn_prefill_varlen(q, k, v, cu, S, Hq, Hkv, D)
-    do, dl = attn.attn_prefill(q, k, v)
+    do, dl = dense_one_range(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o.view(B, Hq, S, D), do)
     assert torch.equal(lse.view(B, Hq, S), dl)
