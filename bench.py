@@ -4,7 +4,9 @@ One step = one causal GQA prefill at long context (batch 1, 8 query heads
 over 2 KV heads, head_dim 128, seq 32768, bf16) followed by one split-K
 decode (batch 32, same heads, per-sequence cache length uniform in
 [256, 4096] from seed 0, bf16), each through the C ABI on torch's current
-stream.  Inputs are seeded synthetic tensors resident in HBM before timing;
+stream, after at least one second of untimed warm-up steps (the GPU's
+clock and power settle over that time).  Inputs are seeded synthetic
+tensors resident in HBM before timing;
 enough input copies are rotated that no launch finds its inputs in the
 256 MB last-level cache.
 
@@ -106,13 +108,10 @@ def measured_traffic():
     return kv
 
 
-def traffic_for(tr, key, workload):
-    """Bytes per launch recorded for ``key`` if they were taken on
-    ``workload``, else None."""
-    if tr.get(key + "_workload") != workload or key + "_hbm_bytes_per_launch" \
-            not in tr:
-        return None
-    return int(tr[key + "_hbm_bytes_per_launch"])
+def traffic_for(tr, workload):
+    """HBM bytes per launch recorded for ``workload``, else None."""
+    key = workload + "_hbm_bytes_per_launch"
+    return int(tr[key]) if key in tr else None
 
 
 def copy_calibration(mbytes, reps=5):
@@ -294,7 +293,22 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
 
 
 
-def time_prefill(attn, inputs, torch, dev, w, steps, warmup):
+def warm_up(run, torch, count, seconds):
+    """run(i) for at least ``count`` calls and at least ``seconds`` of
+    wall time (the GPU's clock and power settle over the first second of
+    sustained load); returns the number of calls."""
+    i = 0
+    t0 = time.perf_counter()
+    while i < count or time.perf_counter() - t0 < seconds:
+        run(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def time_prefill(attn, inputs, torch, dev, w, steps, warmup, warmup_s=0.2):
     """Event-timed launches of one prefill workload through prepared C-ABI
     calls, rotating input copies; returns (stats, copies)."""
     q, k, v = inputs.prefill_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype,
@@ -307,9 +321,7 @@ def time_prefill(attn, inputs, torch, dev, w, steps, warmup):
             for _ in range(R)]
     calls = [attn.prepare_prefill(*ins[r], outs[r], lses[r], causal=w.causal,
                                   scale=w.scale) for r in range(R)]
-    for i in range(warmup):
-        calls[i % R]()
-    torch.cuda.synchronize()
+    warm_up(lambda i: calls[i % R](), torch, warmup, warmup_s)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
           for _ in range(steps)]
     for i in range(steps):
@@ -366,8 +378,11 @@ def prefill_record(w, st, R, traffic=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="least wall time of warm-up steps (the GPU's clock "
+                         "and power settle over the first second)")
     ap.add_argument("--prefill", default="c5_gqa_s32768",
                     help="prefill workload of the step (value / roofline)")
     ap.add_argument("--decode", default="c4_decode_b32")
@@ -441,9 +456,7 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_steps = warm_up(step, torch, args.warmup, args.warmup_seconds)
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -461,7 +474,7 @@ def main():
     side_rec = {}
     for w in side:
         st, R = time_prefill(attn, inputs, torch, dev, w, K, args.warmup)
-        rec = prefill_record(w, st, R)
+        rec = prefill_record(w, st, R, traffic_for(measured_traffic(), w.name))
         rec.update(prefill_launch(attn, w))
         side_rec[w.name] = rec
 
@@ -495,7 +508,7 @@ def main():
     gst = launch_stats([e[0].elapsed_time(e[1]) / Rd for e in gevs])
 
     tr = measured_traffic()
-    prec = prefill_record(wp, pst, Rp, traffic_for(tr, "prefill", wp.name))
+    prec = prefill_record(wp, pst, Rp, traffic_for(tr, wp.name))
     prec.pop("shape")
     prec.update(prefill_launch(attn, wp))
     d_gbs = dbytes / (dst["mean_us"] * 1e-6) / 1e9
@@ -508,6 +521,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_seconds": args.warmup_seconds,
         "ms_per_step": round(wall / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -539,7 +554,7 @@ def main():
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": round(d_gbs / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(tr, "decode", wd.name),
+                "traffic": traffic_for(tr, wd.name),
                 "traffic_unit": "HBM bytes per launch (split + combine)",
                 "bytes_per_launch": dbytes,
                 **dst,
