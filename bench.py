@@ -473,7 +473,8 @@ def main():
     # ---- side configs (other prefill workloads), timed the same way
     side_rec = {}
     for w in side:
-        st, R = time_prefill(attn, inputs, torch, dev, w, K, args.warmup)
+        st, R = time_prefill(attn, inputs, torch, dev, w, K, args.warmup,
+                             min(0.2, args.warmup_seconds))
         rec = prefill_record(w, st, R, traffic_for(measured_traffic(), w.name))
         rec.update(prefill_launch(attn, w))
         side_rec[w.name] = rec

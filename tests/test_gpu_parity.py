@@ -658,7 +658,8 @@ FLAG_BYTES = 4096      # the workspace's flag words, one per pair of tiles
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(4, 8, 2, 2048), (2, 8, 2, 300),
-                                        (1, 16, 4, 1000), (3, 8, 1, 129)])
+                                        (1, 16, 4, 1000), (3, 8, 1, 129),
+                                        (1, 4, 1, 16384)])
 @pytest.mark.parametrize("wait", [-1, 0])
 def test_prefill_balanced_matches_oracle_and_leaves_flags_zero(B, Hq, Hkv, S,
                                                                wait):
