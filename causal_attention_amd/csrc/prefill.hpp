@@ -584,41 +584,46 @@ __device__ __forceinline__ void wg_barrier() {
 
 // ------------------------------------- register-blocked prefill kernel
 //
-// One workgroup of 2 waves per (batch, query head, 128-row query tile), two
-// workgroups per compute unit: one wave per SIMD.  Each wave owns 64 query
-// rows as two 32-row blocks, so every K or V operand read from LDS feeds two
-// MFMAs (half the LDS traffic per MFMA of a 32-row wave).  With 512
-// registers per wave, Q and the output accumulators live in the
-// accumulation registers (AGPRs), which only MFMAs read; scores,
-// probabilities and the K / V operands are VGPRs.  The QK^T products are
-// issued as inline assembly so that the scores land in VGPRs (the compiler
-// otherwise puts every MFMA result in AGPRs and copies the scores back).
+// One wave per SIMD, each owning 64 query rows as two 32-row blocks, so
+// every K or V operand read from LDS feeds two MFMAs (half the LDS traffic
+// per MFMA of a 32-row wave).  With a whole SIMD's 512 registers per lane,
+// Q and the output accumulators live in the accumulation registers (AGPRs),
+// which only MFMAs read; scores, probabilities and the K / V operands are
+// VGPRs.  The QK^T products are issued as inline assembly so that the
+// scores land in VGPRs (the compiler otherwise puts every MFMA result in
+// AGPRs and copies the scores back).  Two forms: four query heads of one KV
+// head per 256-thread workgroup (one wave per head, the same 64 rows; one
+// workgroup per compute unit), or two waves of one head (128 rows; two
+// workgroups per compute unit).
 //
 // Fixed reference.  Each row keeps the max of its first key tile (every row
-// sees key 0) as the reference m of the online softmax of section 2.2 of the
+// sees it) as the reference m of the online softmax of section 2.2 of the
 // attention-fusion page, and never rescales: later probabilities
 // p = 2^(x - m) may exceed 1, and O / l and LSE = m + log2 l are exact for
 // any reference.  While every score stays below m + h, p < 2^h: h = 15 for
 // fp16 probabilities (largest finite value 65504), 32 for bf16 (fp32 sums
-// of p v then overflow only for |v| beyond 2^70); a row whose score goes
-// higher makes the workgroup redo its tile with m set to that row's true
-// max (tracked during the first pass), so that p <= 1 in the second pass.
+// of p v then overflow only for |v| beyond 2^70).  After a pass, a row whose
+// sum l went past 2^h makes the workgroup run its tile again with
+// m + log2 l, an upper bound of the row's scores (see the pass loop).
 // Without a rescale no VALU ever touches the accumulators inside the loop.
 //
-// With no second wave on the SIMD, each wave overlaps its own softmax with
-// its MFMAs through a software pipeline across 32-key tiles (scores
-// double-buffered); per tile i:
-//   A(i): V(i) LDS -> registers; S(i+1) = K(i+1) Q^T  interleaved with
-//         P(i) = exp2(x(i)), l += sum P(i)
-//   B(i): O^T += V(i)^T P(i)^T  interleaved with the row max of S(i+1) and
-//         x(i+1) = S(i+1) c - m; K(i+2) LDS -> registers
-// then a wait for this wave's loads of the next tiles, one barrier (both
-// waves' loads visible, both waves' reads of tile i done) and the direct
-// global -> LDS loads of tile i + NB into tile i's slot.
+// Each wave overlaps its own softmax with its MFMAs through a software
+// pipeline across 32-key tiles (scores double-buffered); per tile i:
+//   A(i): 16 MFMAs of S(i+1) = K(i+1) Q^T, each followed by the
+//         exponentials of one pair of scores of tile i and the packing of
+//         the previous pair; the loads of K(i+5) and V(i+4) spread over
+//         the slots
+//   B(i): 16 MFMAs of O^T += V(i)^T P(i)^T, each followed by a slice of the
+//         row sums of P(i), of the mask of S(i+1) (last tiles only) and of
+//         x(i+1) = S(i+1) c - m; the V(i+1) and K(i+2) operand reads
+// then a wait for this wave's loads of the tiles read next, an LDS wait and
+// one barrier (every wave's loads visible, every wave's reads of the ring
+// slots about to be refilled done).
 //
 // The QK^T products being assembly, the wait states the hardware needs
 // between their results and a VALU read are inserted here (s_nop), with
-// margin over what the compiler emits for the same dependency.
+// margin over what the compiler emits for the same dependency; the build's
+// assembly is checked for AGPR operands rewritten right after such an MFMA.
 constexpr int kRBRing = 4;
 constexpr int kRBMaxPasses = 8;
 // log2 headroom over the reference for probabilities of type T
