@@ -27,11 +27,16 @@ by page title and section:
 * "让编码智能体写 Triton 算子" (zmj.net/articles/3605), step 1: the reference is
   computed in float32 or float64, never in half precision.
 
+``residual_rmsnorm`` and ``prefill_residual_rmsnorm`` (``oracle/epilogue.py``)
+add a residual to the attention output and RMS-normalise each head row, the
+fused epilogue of the "triton-optimization" skill page, section 3.2.
+
 ``rope`` (``oracle/rotary.py``) rotates q and k before attention, following the
 "triton-optimization" skill page, section 3.4 (fused RoPE: rotate pairs
 (x[i], x[i + D/2]) by position-dependent angles).
 
-Pinned by ``tests/test_oracle.py`` and ``tests/test_oracle_rope.py`` (closed
+Pinned by ``tests/test_oracle.py``, ``tests/test_oracle_rope.py`` and
+``tests/test_oracle_epilogue.py`` (closed
 forms, brute force on tiny inputs, an fp64 library implementation, algebraic
 invariants, planted mistakes).  No function here is "parity unpinned".
 """
@@ -46,3 +51,4 @@ from .attention import (  # noqa: F401
     softmax_probabilities,
 )
 from .rotary import rope  # noqa: F401
+from .epilogue import residual_rmsnorm, prefill_residual_rmsnorm  # noqa: F401
