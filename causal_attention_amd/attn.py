@@ -89,9 +89,14 @@ def lib():
         L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f,
                                           i, vp, vp]
         L.attn_decode_noalloc.restype = i
+        L.attn_prefill_residual_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp,
+                                                    vp, i, i, i, i, i, f, i,
+                                                    f, vp]
+        L.attn_prefill_residual_rmsnorm.restype = i
         for n in ("attn_prefill_rope_f16", "attn_prefill_varlen_f16",
                   "attn_prefill_padded_f16", "attn_kv_append_f16",
-                  "attn_decode_padded_f16"):
+                  "attn_decode_padded_f16",
+                  "attn_prefill_residual_rmsnorm_f16"):
             fn, base = getattr(L, n), getattr(L, n[:-4])
             fn.argtypes, fn.restype = base.argtypes, base.restype
         L.attn_status_string.argtypes = [i]
@@ -476,6 +481,40 @@ def attn_prefill_padded(q, k, v, seqlens, causal=True, scale=None, out=None,
     st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                               _ptr(lse), _ptr(seqlens), B, Hq, Hkv, S, D,
                               float(scale), int(bool(causal)), _stream())
+    if st != 0:
+        raise AttnError(st, name)
+    return out, lse
+
+
+def attn_prefill_residual_rmsnorm(q, k, v, residual, weight, eps=1e-6,
+                                  causal=True, scale=None, out=None,
+                                  lse=None, with_lse=True):
+    """Prefill with the fused residual add + RMSNorm epilogue (bf16 or fp16).
+
+    q, residual [B,Hq,S,D]; k, v [B,Hkv,S,D]; weight [D]; all of q's dtype.
+    For each head row: x = attention output + residual, out = x /
+    sqrt(mean(x^2) + eps) * weight.  ``residual`` is overwritten with x.
+    Returns (out, lse).
+    """
+    name = _fn("attn_prefill_residual_rmsnorm", q.dtype)
+    B, Hq, Hkv, S, D = _prefill_shapes(q, k, v, q.dtype)
+    _check(residual, "residual", q.dtype, 4)
+    _shape(residual, "residual", q.shape)
+    _check(weight, "weight", q.dtype, 1)
+    _shape(weight, "weight", (D,))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.dtype, 4)
+    _shape(out, "out", q.shape)
+    lse = _lse_arg(lse, with_lse, (B, Hq, S), q)
+    _on_gpu(q=q, k=k, v=v, residual=residual, weight=weight, out=out,
+            lse=lse)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(residual),
+                              _ptr(weight), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                              S, D, float(scale), int(bool(causal)),
+                              float(eps), _stream())
     if st != 0:
         raise AttnError(st, name)
     return out, lse

@@ -1,6 +1,7 @@
 // C-ABI entry points of libattn.so: host-side validation, tile choice and
 // kernel launches.  Declarations and the contract live in include/attn.h.
 #include "attn.h"
+#include "attn_debug.h"
 
 #include <hip/hip_runtime.h>
 
@@ -209,7 +210,7 @@ struct Half16Prefill {
       }
       hipLaunchKernelGGL((attn::attn_prefill_kernel<T, D, C>), g, b, 0, st, q,
                          k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu, use_rope,
-                         rope, cu_seqlens, seq_lens);
+                         rope, cu_seqlens, seq_lens, attn::RmsEpilogue<T>{});
     }
   };
 };
@@ -336,6 +337,46 @@ int prefill16(const void* q, const void* k, const void* v, void* o,
       static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv, S, D,
       scale, causal, stream, 0, attn::RopeRates{}, nullptr, nullptr,
       split_ws);
+}
+
+// Prefill with the residual-add + RMSNorm epilogue: the 4-wave kernel with
+// its RMS flag, dense [B, H, S, D] tensors, any shape the prefill accepts.
+template <typename T>
+int prefill16_rms(const void* q, const void* k, const void* v,
+                  void* residual, const void* weight, void* out, float* lse,
+                  int B, int Hq, int Hkv, int S, int D, float scale,
+                  int causal, float eps, void* stream) {
+  bool empty;
+  const int st = check_prefill(q, k, v, out, lse, B, Hq, Hkv, S, D, scale,
+                               &empty);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(eps) || !(eps >= 0.f)) return ATTN_ERR_SCALE;
+  if (empty) return ATTN_OK;
+  if (!residual || !weight) return ATTN_ERR_NULL;
+  if (!aligned(residual, 16) || !aligned(weight, 16)) return ATTN_ERR_ALIGN;
+  if (residual == out) return ATTN_ERR_SHAPE;   // x and y need their own rows
+  const int nq = (S + kPrefillBM - 1) / kPrefillBM;
+  const dim3 g((unsigned)(B * Hq * nq)), b(kPrefillThreads);
+  const float sl2 = scale * attn::kLog2e;
+  const int ncu = device_cu_count();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const T *qt = static_cast<const T*>(q), *kt = static_cast<const T*>(k),
+          *vt = static_cast<const T*>(v);
+  T* ot = static_cast<T*>(out);
+  const attn::RmsEpilogue<T> rms{static_cast<T*>(residual),
+                                 static_cast<const T*>(weight), eps};
+  const attn::RopeRates rope{};
+#define ATTN_RMS_LAUNCH(DD, CC)                                               \
+  hipLaunchKernelGGL((attn::attn_prefill_kernel<T, DD, CC, true>), g, b, 0,  \
+                     hs, qt, kt, vt, ot, lse, B, Hq, Hkv, S, sl2, nq, ncu, 0, \
+                     rope, nullptr, nullptr, rms)
+  if (D == 64) {
+    if (causal) ATTN_RMS_LAUNCH(64, true); else ATTN_RMS_LAUNCH(64, false);
+  } else {
+    if (causal) ATTN_RMS_LAUNCH(128, true); else ATTN_RMS_LAUNCH(128, false);
+  }
+#undef ATTN_RMS_LAUNCH
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 // Shared body of the decode entry points; cap = 0 for the packed cache, else
@@ -618,6 +659,26 @@ int attn_prefill_padded_f16(const void* q, const void* k, const void* v,
                                     D, scale, causal, stream);
 }
 
+int attn_prefill_residual_rmsnorm(const void* q, const void* k,
+                                  const void* v, void* residual,
+                                  const void* weight, void* out, float* lse,
+                                  int B, int Hq, int Hkv, int S, int D,
+                                  float scale, int causal, float eps,
+                                  void* stream) {
+  return prefill16_rms<__bf16>(q, k, v, residual, weight, out, lse, B, Hq,
+                               Hkv, S, D, scale, causal, eps, stream);
+}
+
+int attn_prefill_residual_rmsnorm_f16(const void* q, const void* k,
+                                      const void* v, void* residual,
+                                      const void* weight, void* out,
+                                      float* lse, int B, int Hq, int Hkv,
+                                      int S, int D, float scale, int causal,
+                                      float eps, void* stream) {
+  return prefill16_rms<_Float16>(q, k, v, residual, weight, out, lse, B, Hq,
+                                 Hkv, S, D, scale, causal, eps, stream);
+}
+
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
                      float* lse, int B, int Hq, int Hkv, int S, int D,
                      float scale, int causal, void* stream) {
@@ -722,6 +783,19 @@ int attn_kv_append_f16(const void* k_new, const void* v_new, void* kcache,
   return kv_append16<_Float16>(k_new, v_new, kcache, vcache, seqlens, B, Hkv,
                                D, cap, rope_base, stream);
 }
+
+#ifdef ATTN_DEBUG_TRACE
+int attn_debug_trace(int b, int h, int row, float* buf, int capacity) {
+  if (buf != nullptr && (b < 0 || h < 0 || row < 0 || capacity < 0))
+    return ATTN_ERR_SHAPE;
+  if (!aligned(buf, 4)) return ATTN_ERR_ALIGN;
+  const attn::TraceTarget t{buf, b, h, row, capacity};
+  return hipMemcpyToSymbol(HIP_SYMBOL(attn::g_trace), &t, sizeof t) ==
+                 hipSuccess
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+#endif
 
 const char* attn_status_string(int status) {
   switch (status) {

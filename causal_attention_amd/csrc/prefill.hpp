@@ -29,6 +29,39 @@
 
 namespace attn {
 
+#ifdef ATTN_DEBUG_TRACE
+// Debug builds only (libattn_debug.so): the online-softmax state of one
+// chosen query row after every key tile of the 4-wave and fp32 prefill
+// kernels, for comparison with the reference's state at the same key count
+// (the debugging practice of the attention-fusion page, section 6.3).
+// Record jt of the target row holds {keys covered so far, m in natural-log
+// units of the scaled scores, l = sum of exp(s - m) over those keys}.
+struct TraceTarget {
+  float* buf;      // device, 3 * cap floats; NULL: tracing off
+  int b, h, row, cap;
+};
+__device__ TraceTarget g_trace;
+
+// Called by every lane after tile jt (the exchange of the lane-partial sum
+// needs both halves of the wave); only the target row's lane writes.
+__device__ __forceinline__ void trace_tile(int b, int h, int row, int hh,
+                                           int jt, int keys, float m_log2,
+                                           float l_lane) {
+  const float l = l_lane + __shfl_xor(l_lane, 32, 64);
+  const TraceTarget t = g_trace;
+  if (t.buf != nullptr && hh == 0 && b == t.b && h == t.h && row == t.row &&
+      jt < t.cap) {
+    float* r = t.buf + 3 * (size_t)jt;
+    r[0] = (float)keys;
+    r[1] = m_log2 * 0.6931471805599453f;
+    r[2] = l;
+  }
+}
+#define ATTN_TRACE_TILE(...) trace_tile(__VA_ARGS__)
+#else
+#define ATTN_TRACE_TILE(...) ((void)0)
+#endif
+
 constexpr int kPrefillThreads = 256;   // 4 waves
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
@@ -294,13 +327,27 @@ __device__ __forceinline__ void lds_buffer_load16_at(const u32x4& rsrc,
 // s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T, int D, bool CAUSAL>
+// Residual add and RMSNorm fused into the 4-wave kernel's epilogue (the
+// fused RMSNorm-with-residual of the "triton-optimization" page, section
+// 3.2, applied to each query row of one head, the next extension named by
+// section 6.3 of the attention-fusion page): x = o + residual with o the
+// attention row before rounding, y = x / sqrt(mean(x^2) + eps) * w.  y goes
+// to O and x back into the residual buffer, both rounded to nearest even.
+template <typename T>
+struct RmsEpilogue {
+  T* resid;        // [B, Hq, S, D]: read, then overwritten with x
+  const T* w;      // [D]
+  float eps;
+};
+
+template <typename T, int D, bool CAUSAL, bool RMS = false>
 __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
     float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
-    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens) {
+    const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens,
+    RmsEpilogue<T> rms) {
   constexpr int BM = kPrefillBM, BN = 64, NKB = BN / 32, NDB = D / 32;
   constexpr int KT = D / 16;                  // MFMA k-steps over D
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -533,6 +580,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     T* nxt = smem + (buf ^ 1) * 2 * TILE;
     if (jt + 1 < n_kv) issue_tile(jt + 1, nxt, nxt + TILE);
     tile_body(mask_tag, jt * BN, cur, cur + TILE);
+    ATTN_TRACE_TILE(tc.b, tc.hq, query, hh, jt, min((jt + 1) * BN, S), m_i,
+                    l_i);
   };
   if (n_kv > 0) issue_tile(0, smem, smem + TILE);
   // Two tiles per iteration so that the buffer of each is a constant.
@@ -545,7 +594,58 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
 
   // Epilogue: O = acc / l (input type, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
-  if (query < S) {
+  if constexpr (RMS) {
+    // Lane `query` (hh = 0) and its partner in the other half (hh = 1) hold
+    // the row's D values between them: dims 32db + 8a + 4hh + 0..3.  Both
+    // run the exchange of the squared sums; rows past S only skip memory.
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const bool live = query < S;
+    const float inv = 1.f / l_tot;
+    const size_t row = q_row0 + (live ? query : 0);
+    T* xrow = rms.resid + row * D;
+    float ss = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 rr = u32x2{};
+        if (live)
+          rr = *reinterpret_cast<const u32x2*>(xrow + db * 32 + 8 * a +
+                                               4 * hh);
+        const t4 r4 = __builtin_bit_cast(t4, rr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = oacc[db][4 * a + e] * inv + (float)r4[e];
+          oacc[db][4 * a + e] = x;
+          ss = fmaf(x, x, ss);
+        }
+      }
+    ss += swap_halves(ss);
+    const float rs = 1.f / sqrtf(ss * (1.f / D) + rms.eps);
+    if (live) {
+      T* orow = O + row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int col = db * 32 + 8 * a + 4 * hh;
+          const u32x2 wr = *reinterpret_cast<const u32x2*>(rms.w + col);
+          const t4 w4 = __builtin_bit_cast(t4, wr);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * a + e];
+          u32x2 py, px;
+          py[0] = E::pack2(x[0] * rs * (float)w4[0], x[1] * rs * (float)w4[1]);
+          py[1] = E::pack2(x[2] * rs * (float)w4[2], x[3] * rs * (float)w4[3]);
+          px[0] = E::pack2(x[0], x[1]);
+          px[1] = E::pack2(x[2], x[3]);
+          *reinterpret_cast<u32x2*>(orow + col) = py;
+          *reinterpret_cast<u32x2*>(xrow + col) = px;
+        }
+      if (LSE != nullptr && hh == 0)
+        LSE[q_row0 + query] = (m_i + fast_log2(l_tot)) * kLn2;
+    }
+  } else if (query < S) {
     const float inv = 1.f / l_tot;
     T* orow = O + (q_row0 + query) * D;
 #pragma unroll
@@ -1588,6 +1688,7 @@ __global__ __launch_bounds__(kPrefillThreads) void attn_prefill_f32_kernel(
     if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > wq0))
       apply_mask<NKB, CAUSAL>(sacc, j0, hh, query, S);
     softmax_step<NKB, NDB>(sacc, scale_log2, m_i, l_i, oacc);
+    ATTN_TRACE_TILE(tc.b, tc.hq, query, hh, jt, min(j0 + BN, S), m_i, l_i);
 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)

@@ -82,6 +82,16 @@ def prefill_inputs(B, Hq, Hkv, S, D, dtype="bf16", sigma=1.0, seed=0):
     return _round(q, dtype), _round(k, dtype), _round(v, dtype)
 
 
+def residual_inputs(B, Hq, S, D, dtype="bf16", sigma=1.0, seed=0):
+    """The residual-add + RMSNorm epilogue's extra inputs: a residual
+    [B,Hq,S,D] ~ N(0, sigma^2) and a weight [D] = 1 + N(0, 0.25^2), drawn
+    from ``default_rng([2, seed])`` (apart from the q, k, v stream)."""
+    rng = np.random.default_rng([2, seed])
+    r = rng.standard_normal((B, Hq, S, D), dtype=np.float32) * np.float32(sigma)
+    w = 1.0 + 0.25 * rng.standard_normal(D, dtype=np.float32)
+    return _round(r, dtype), _round(w, dtype)
+
+
 def decode_seqlens(B, lmin, lmax, seed=0):
     """Per-sequence cache lengths, uniform on [lmin, lmax] inclusive."""
     rng = np.random.default_rng(seed)

@@ -49,7 +49,8 @@ typedef enum {
   ATTN_ERR_SPLITS = -7,    /* num_splits < 0 or > ATTN_MAX_SPLITS */
   ATTN_ERR_LAUNCH = -8,    /* the HIP runtime rejected a kernel launch */
   ATTN_ERR_SCALE = -9      /* scale is not a finite positive number (or a
-                              RoPE base is negative or not finite) */
+                              RoPE base or an RMSNorm eps is negative or
+                              not finite) */
 } attn_status;
 
 /* Largest num_splits attn_decode accepts. */
@@ -218,6 +219,44 @@ int attn_prefill_padded_f16(const void* q, const void* k, const void* v,
                             void* o, float* lse, const int* seqlens, int B,
                             int Hq, int Hkv, int S, int D, float scale,
                             int causal, void* stream);
+
+/*
+ * Prefill attention with a fused residual add and RMSNorm on its output, bf16
+ * storage: the fused RMSNorm-with-residual of the "triton-optimization" page
+ * (section 3.2; the same forward as "第 6 讲：核函数与 Triton", section 9.1)
+ * applied in the attention kernel's epilogue, the extension named by the
+ * attention-fusion page, section 6.3.  For each query row of each head, with
+ * o the attention output row (fp32, before rounding):
+ *   x = o + residual[b, h, i, :]
+ *   out[b, h, i, :] = x / sqrt(mean_d(x^2) + eps) * weight
+ *   residual[b, h, i, :] = x            (in place, for the next layer)
+ *   q, out, residual : [B, Hq, S, D] bf16    k, v : [B, Hkv, S, D] bf16
+ *   weight : [D] bf16    lse : [B, Hq, S] fp32 (the attention's), or NULL
+ *   eps    : >= 0 and finite (the pages' default is 1e-6; with eps = 0 an
+ *            all-zero row x gives NaN)
+ * The row normalised is one head's D values.  Always the 4-wave prefill
+ * kernel; other arguments as attn_prefill.  Errors as attn_prefill, plus:
+ * residual or weight NULL -> ATTN_ERR_NULL; either not 16-byte aligned ->
+ * ATTN_ERR_ALIGN; eps negative or not finite -> ATTN_ERR_SCALE; residual ==
+ * out -> ATTN_ERR_SHAPE.
+ */
+int attn_prefill_residual_rmsnorm(const void* q, const void* k,
+                                  const void* v, void* residual,
+                                  const void* weight, void* out, float* lse,
+                                  int B, int Hq, int Hkv, int S, int D,
+                                  float scale, int causal, float eps,
+                                  void* stream);
+
+/*
+ * attn_prefill_residual_rmsnorm with fp16 storage (q, k, v, residual, weight
+ * and out in IEEE fp16).  Same arguments, layouts and errors.
+ */
+int attn_prefill_residual_rmsnorm_f16(const void* q, const void* k,
+                                      const void* v, void* residual,
+                                      const void* weight, void* out,
+                                      float* lse, int B, int Hq, int Hkv,
+                                      int S, int D, float scale, int causal,
+                                      float eps, void* stream);
 
 /*
  * Prefill attention, fp32 storage.  Same arguments and layouts as

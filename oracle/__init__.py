@@ -49,6 +49,7 @@ from .attention import (  # noqa: F401
     decode,
     lse_combine,
     softmax_probabilities,
+    prefix_softmax_state,
 )
 from .rotary import rope  # noqa: F401
 from .epilogue import residual_rmsnorm, prefill_residual_rmsnorm  # noqa: F401

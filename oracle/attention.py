@@ -253,3 +253,31 @@ def lse_combine(o_parts, lse_parts):
     with np.errstate(divide="ignore"):
         lse = np.where(empty, -np.inf, M_safe + np.log(W_safe))
     return o, lse
+
+
+def prefix_softmax_state(q, k, scale, causal, b, h, row, key_counts):
+    """The softmax state of one query row after its first n keys.
+
+    This is the intermediate state that the online softmax of
+    "Attention三算子融合实战" section 2.2 carries from block to block: after the
+    keys 0 .. n-1 have been seen, the row max m_n of the visible scores among
+    them and their log-sum-exp lse_n = m_n + ln(sum_j exp(s_j - m_n)).  Section
+    6.3 of the same page compares a kernel's per-iteration m_i and l_i with
+    the reference's values at the same positions; this gives those values.
+    q [B,Hq,S,D], k [B,Hkv,S,D]; key_counts: iterable of n (0 <= n <= S).
+    Returns (m [len], lse [len]) in float64; -inf where no key is visible.
+    """
+    q, k = _f64(q), _f64(k)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _check_heads(Hq, Hkv)
+    g = _kv_head(h, Hq, Hkv)
+    s = scale * (k[b, g] @ q[b, h, row])                 # the score row [S]
+    vis_row = _visible(np.array([row]), S, causal)[0]
+    ms, lses = [], []
+    for n in key_counts:
+        vis = vis_row & (np.arange(S) < n)
+        _, lse = _two_pass_softmax(s[None, :], vis[None, :])
+        ms.append(np.where(vis, s, -np.inf).max(initial=-np.inf))
+        lses.append(lse[0])
+    return np.array(ms), np.array(lses)

@@ -34,6 +34,8 @@ def test_header_declares_the_entry_points():
               "attn_prefill_select", "attn_prefill_kernel_for",
               "attn_prefill_ws", "attn_prefill_ws_f16",
               "attn_prefill_workspace_size", "attn_prefill_split_wait",
+              "attn_prefill_residual_rmsnorm",
+              "attn_prefill_residual_rmsnorm_f16",
               "attn_status_string"]:
         assert n in names
 
@@ -42,6 +44,21 @@ def test_library_exports_every_declared_symbol():
     L = attn.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
+
+
+def test_debug_library_exports_the_trace_and_every_declared_symbol():
+    from causal_attention_amd import debug
+    L = debug.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert hasattr(L, "attn_debug_trace")
+    # the release library has no trace
+    assert not hasattr(attn.lib(), "attn_debug_trace")
+    # argument errors are found before any HIP call
+    assert L.attn_debug_trace(-1, 0, 0, A, 4) == -2
+    assert L.attn_debug_trace(0, 0, -3, A, 4) == -2
+    assert L.attn_debug_trace(0, 0, 0, A, -1) == -2
+    assert L.attn_debug_trace(0, 0, 0, A + 2, 4) == -5
 
 
 def test_status_strings():
@@ -337,6 +354,36 @@ def test_prefill_padded_argument_errors(fn):
     assert prefill_padded(S=0, q=None, k=None, v=None, o=None, sl=None) == 0
 
 
+def prefill_rms(q=A, k=A, v=A, res=A + 0x100, w=A + 0x200, o=A + 0x300,
+                lse=None, B=1, Hq=8, Hkv=2, S=64, D=128, scale=0.1, causal=1,
+                eps=1e-6, fn="attn_prefill_residual_rmsnorm"):
+    return getattr(attn.lib(), fn)(q, k, v, res, w, o, lse, B, Hq, Hkv, S, D,
+                                   scale, causal, eps, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_prefill_residual_rmsnorm",
+                                "attn_prefill_residual_rmsnorm_f16"])
+def test_prefill_residual_rmsnorm_argument_errors(fn):
+    import functools
+    f = functools.partial(prefill_rms, fn=fn)
+    assert f(res=None) == -1
+    assert f(w=None) == -1
+    assert f(q=None) == -1
+    assert f(res=A + 8) == -5
+    assert f(w=A + 8) == -5
+    assert f(o=A + 0x100) == -2          # residual and out are one buffer
+    assert f(eps=-1e-6) == -9
+    assert f(eps=float("inf")) == -9
+    assert f(eps=float("nan")) == -9
+    assert f(scale=0.0) == -9
+    assert f(D=96) == -4
+    assert f(Hq=8, Hkv=3) == -3
+    assert f(S=-1) == -2
+    assert f(B=0, q=None, k=None, v=None, res=None, w=None, o=None) == 0
+    assert f(S=0, q=None, k=None, v=None, res=None, w=None, o=None) == 0
+    assert f(B=0, eps=-1.0) == -9       # eps is checked even when empty
+
+
 def test_decode_argument_errors_detail():
     assert decode(B=-1) == -2
     assert decode(Hq=8, Hkv=3) == -3
@@ -433,6 +480,18 @@ def test_binding_checks_prefill_output_shapes():
             torch.zeros(2, dtype=torch.int32))
     _raises("bfloat16 or float16", attn.attn_prefill_rope,
             q.float(), k.float(), k.float(), 1e4)
+    w = _t(128)
+    _raises("residual must have shape", attn.attn_prefill_residual_rmsnorm,
+            q, k, k, _t(1, 8, 32, 128), w)
+    _raises("weight must have shape", attn.attn_prefill_residual_rmsnorm,
+            q, k, k, _t(1, 8, 64, 128), _t(64))
+    _raises("out must have shape", attn.attn_prefill_residual_rmsnorm,
+            q, k, k, _t(1, 8, 64, 128), w, out=_t(1, 8, 64, 64))
+    _raises("residual must be torch.float16",
+            attn.attn_prefill_residual_rmsnorm, q.half(), k.half(), k.half(),
+            _t(1, 8, 64, 128), w.half())
+    _raises("GPU tensor", attn.attn_prefill_residual_rmsnorm, q, k, k,
+            _t(1, 8, 64, 128), w)
 
 
 def test_binding_checks_decode_output_shapes():

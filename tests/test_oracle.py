@@ -479,3 +479,56 @@ def test_padded_rows_and_content():
             assert (o[b, :, L:] == 0).all() and (lse[b, :, L:] == -np.inf).all()
             assert np.array_equal(o2[b, :, :L], o[b, :, :L])
             assert np.array_equal(lse2[b, :, :L], lse[b, :, :L])
+
+
+# ---------------------------------------- per-key-prefix softmax state (trace)
+
+def test_prefix_state_full_prefix_equals_the_row_lse():
+    q, k, v = prefill_np(2, 4, 2, 40, 16, seed=21)
+    _, lse = oracle.prefill(q, k, v, 0.3, True)
+    _, lse_f = oracle.prefill(q, k, v, 0.3, False)
+    for b, h, row in [(0, 0, 0), (1, 3, 17), (0, 2, 39)]:
+        m, l = oracle.prefix_softmax_state(q, k, 0.3, True, b, h, row,
+                                           [row + 1, 40])
+        np.testing.assert_allclose(l, lse[b, h, row], atol=TOL)
+        _, lf = oracle.prefix_softmax_state(q, k, 0.3, False, b, h, row,
+                                            [40])
+        np.testing.assert_allclose(lf, lse_f[b, h, row], atol=TOL)
+
+
+def test_prefix_state_first_key_and_empty_prefix():
+    q, k, _ = prefill_np(1, 4, 2, 12, 8, seed=22)
+    for h in range(4):
+        m, l = oracle.prefix_softmax_state(q, k, 0.5, True, 0, h, 7, [0, 1])
+        s0 = 0.5 * q[0, h, 7] @ k[0, h // 2, 0]
+        assert m[0] == -np.inf and l[0] == -np.inf
+        np.testing.assert_allclose([m[1], l[1]], [s0, s0], atol=TOL)
+
+
+def test_prefix_state_identical_keys_closed_form():
+    q, k, _ = prefill_np(1, 2, 1, 20, 8, seed=23)
+    k[:] = k[:, :, :1, :]
+    n = np.arange(1, 21)
+    for causal in (True, False):
+        m, l = oracle.prefix_softmax_state(q, k, 0.2, causal, 0, 1, 9, n)
+        s = 0.2 * q[0, 1, 9] @ k[0, 0, 0]
+        seen = np.minimum(n, 10) if causal else n
+        np.testing.assert_allclose(m, s, atol=TOL)
+        np.testing.assert_allclose(l, s + np.log(seen), atol=TOL)
+
+
+def test_prefix_state_brute_force():
+    q, k, _ = prefill_np(1, 2, 2, 9, 4, seed=24)
+    row = 6
+    m, l = oracle.prefix_softmax_state(q, k, 0.7, True, 0, 1, row,
+                                       range(10))
+    for n in range(10):
+        ss = [0.7 * sum(q[0, 1, row, d] * k[0, 1, j, d] for d in range(4))
+              for j in range(min(n, row + 1))]
+        if not ss:
+            assert m[n] == -np.inf and l[n] == -np.inf
+            continue
+        mx = max(ss)
+        assert abs(m[n] - mx) <= TOL
+        assert abs(l[n] - (mx + math.log(sum(math.exp(x - mx)
+                                                for x in ss)))) <= TOL
