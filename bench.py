@@ -20,7 +20,8 @@ and minimum launch time.  ``side_configs`` times the other prefill workloads
 (batch 4 at seq 2048 by default) the same way, each against its own dtype's
 peak.  ``cpu_baseline`` times the fp64 CPU oracle on the host on a bounded
 sample of the same workload.  With ``--extras`` the line also carries
-``extras``: the widened paths (fp16 storage, RoPE, ragged batch) timed on
+``extras``: the widened paths (fp16 storage, RoPE, ragged batch, the fused
+residual + RMSNorm epilogue) timed on
 the shapes of the batch-4 prefill and the decode.
 """
 
@@ -295,6 +296,27 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
         lambda: attn.attn_prefill_padded(qp, kp2, vp2, slp, out=op,
                                          with_lse=False)))
     out["prefill_padded"]["sequences"] = f"the same {B} lengths, padded to {Smax} rows"
+
+    # residual add + RMSNorm fused into the 4-wave kernel's epilogue, beside
+    # the plain 4-wave prefill on the same inputs (the fused path adds a read
+    # and a write of the residual and a read of the weight)
+    res, wgt = (t.to(dev) for t in inputs.residual_inputs(
+        wp.B, wp.Hq, wp.S, wp.D, "bf16", 1.0, wp.seed))
+    orms = torch.empty_like(qb)
+    out["prefill_residual_rmsnorm"] = tf(flops, timed(
+        lambda: attn.attn_prefill_residual_rmsnorm(qb, kb, vb, res, wgt,
+                                                   out=orms,
+                                                   with_lse=False)))
+    prev = attn.prefill_select(attn.PREFILL_W4)
+    prev_ws = attn.prefill_workspace_policy(False)
+    try:
+        out["prefill_w4_plain"] = tf(flops, timed(
+            lambda: attn.attn_prefill(qb, kb, vb, out=ob, with_lse=False)))
+    finally:
+        attn.prefill_select(prev)
+        attn.prefill_workspace_policy(prev_ws)
+    out["prefill_residual_rmsnorm"]["extra_bytes"] = int(
+        2 * res.numel() * res.element_size() + wgt.numel() * 2)
     return out
 
 

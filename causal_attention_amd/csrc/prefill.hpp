@@ -775,9 +775,10 @@ __device__ __forceinline__ void mfma_to_valu_wait(f32x16& s0, f32x16& s1) {
 // 64-row query tiles all run at once (one workgroup per compute unit).
 // Query tile t needs n_t key tiles, growing with t, so with one tile per
 // compute unit the launch lasts as long as its last tile.  Instead tiles
-// l and nq-1-l are paired and their n_l + n_h key tiles are cut evenly
-// between two workgroups: A runs key tiles 0 .. c-1 of the heavy tile h,
-// c = (n_h - n_l) / 2, leaves that partial state (unnormalised O, reference
+// l and nq-1-l are paired and their n_l + n_h key tiles are cut about
+// evenly between two workgroups: A runs key tiles 0 .. c-1 of the heavy
+// tile h, c = (n_h - n_l) / 2 - kRBCutShift (at least 0; A's fixed costs are
+// the larger), leaves that partial state (unnormalised O, reference
 // m, row sums l, lane by lane) in the workspace and then runs tile l whole;
 // B runs key tiles c .. n_h-1 of tile h and merges A's part into its own
 // before it writes tile h (two key ranges of one row merged with their
@@ -867,6 +868,12 @@ __host__ __device__ __forceinline__ int rb_causal_tiles(int t, int S) {
 // workspace serves launches of any sizes), then per pair, wave and 16-byte
 // chunk (32 of O, one of m and l) the 64 lanes' values.
 constexpr int kRBDumpChunks = 33;
+// Key tiles moved from A's share of the heavy tile to B's: besides its key
+// tiles, A pays a second job start and its part's stores (about 6 us on
+// MI355X), B the wait and the merge (about 4 us), so an even cut leaves A
+// last.  Measured on the batch-4 seq-2048 launch (bf16, 8/2 heads): shifts
+// 0 / 1 / 2 / 3 / 4 ran 52.4 / 51.3 / 51.0 / 51.6 / 52.3 us mean.
+constexpr int kRBCutShift = 2;
 constexpr int kRBFlagBytes = 4096;
 constexpr int kRBMaxPairs = kRBFlagBytes / 4;
 __host__ __device__ __forceinline__ size_t rb_split_bytes(long long np) {
@@ -1373,9 +1380,11 @@ void attn_prefill_rb_kernel(
                       ((size_t)pidx * WAVES + w) * (kRBDumpChunks * 64 * 4);
   if constexpr (SPLIT) {
     {
-      const int c = sc.role == 2 ? 0
-                                 : (rb_causal_tiles(qt_h, S) -
-                                    rb_causal_tiles(sc.pair, S)) / 2;
+      const int c = sc.role == 2
+                        ? 0
+                        : max(0, (rb_causal_tiles(qt_h, S) -
+                                  rb_causal_tiles(sc.pair, S)) / 2 -
+                                     kRBCutShift);
       if (sc.role == 0 && c > 0) {
         jq = qt_h;
         jhi = c;
