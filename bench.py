@@ -370,12 +370,16 @@ def prefill_launch(attn, w):
     kern, wgs, thr = attn.prefill_workgroups(w.B, w.Hq, w.Hkv, w.S, w.D,
                                              w.causal)
     balanced = attn.prefill_balanced(w.B, w.Hq, w.Hkv, w.S, w.D, w.causal)
+    if balanced:
+        schedule = ("balanced: query tiles t and n-1-t paired, each pair's "
+                    "key tiles cut between two workgroups")
+    elif kern == attn.PREFILL_KS:
+        schedule = ("key split: 32 query rows per workgroup, its four waves "
+                    "take every fourth key tile and merge in LDS")
+    else:
+        schedule = "one workgroup per query tile, heaviest first"
     return {"kernel": attn.PREFILL_KERNEL_NAMES[kern], "workgroups": wgs,
-            "threads": thr,
-            "schedule": ("balanced: query tiles t and n-1-t paired, each "
-                         "pair's key tiles cut evenly between two "
-                         "workgroups" if balanced else
-                         "one workgroup per query tile, heaviest first")}
+            "threads": thr, "schedule": schedule}
 
 
 def prefill_record(w, st, R, traffic=None):

@@ -660,14 +660,15 @@ def prepare_decode(q, kcache, vcache, seqlens, out, Hkv, workspace,
                                lse))
 
 
-PREFILL_AUTO, PREFILL_W4, PREFILL_RB = 0, 1, 2
+PREFILL_AUTO, PREFILL_W4, PREFILL_RB, PREFILL_KS = 0, 1, 2, 3
 PREFILL_KERNEL_NAMES = {PREFILL_W4: "attn_prefill_kernel",
-                        PREFILL_RB: "attn_prefill_rb_kernel"}
+                        PREFILL_RB: "attn_prefill_rb_kernel",
+                        PREFILL_KS: "attn_prefill_ks_kernel"}
 
 
 def prefill_select(kernel):
     """Process-wide choice of the 16-bit prefill kernel (PREFILL_AUTO,
-    PREFILL_W4 or PREFILL_RB); returns the previous one."""
+    PREFILL_W4, PREFILL_RB or PREFILL_KS); returns the previous one."""
     prev = int(lib().attn_prefill_select(int(kernel)))
     if prev < 0:
         raise ValueError(f"attn_prefill_select({kernel}): "
@@ -676,8 +677,8 @@ def prefill_select(kernel):
 
 
 def prefill_kernel_for(B, Hq, S, D, causal=True):
-    """PREFILL_W4 or PREFILL_RB: the kernel a 16-bit prefill launch of these
-    sizes uses under the current setting."""
+    """PREFILL_W4, PREFILL_RB or PREFILL_KS: the kernel a dense 16-bit
+    prefill launch of these sizes uses under the current setting."""
     return int(lib().attn_prefill_kernel_for(int(B), int(Hq), int(S), int(D),
                                              int(bool(causal))))
 
@@ -695,6 +696,8 @@ def prefill_workgroups(B, Hq, Hkv, S, D, causal=True):
     if prefill_balanced(B, Hq, Hkv, S, D, causal):
         return PREFILL_RB, B * (Hq // 4) * -(-S // 64), 256
     kern = prefill_kernel_for(B, Hq, S, D, causal)
+    if kern == PREFILL_KS:
+        return kern, B * Hq * -(-S // 32), 256
     if kern == PREFILL_RB and (Hq // Hkv) % 4 == 0:
         return kern, B * (Hq // 4) * -(-S // 64), 256
     if kern == PREFILL_RB:

@@ -12,6 +12,7 @@
 #include "decode.hpp"
 #include "kvcache.hpp"
 #include "prefill.hpp"
+#include "prefill_ks.hpp"
 
 namespace {
 
@@ -135,6 +136,29 @@ bool prefill_use_rb(int B, int Hq, int S, int D, int causal) {
   return work >= 4e8;
 }
 
+// The key-split kernel (attn_prefill_ks_kernel: four waves share 32 query
+// rows and split their key tiles) for dense launches too small to fill the
+// GPU, where the other kernels' launches last as long as the key chain of
+// their last query rows: its grid, B Hq ceil(S/32) workgroups of one per
+// compute unit, must fit in two rounds.  Measured on MI355X (bf16, mean of
+// 300 launches, us, key-split against the automatic choice before it):
+// B1 12/12 S512 D64 causal 10.3 / 13.6 (full 9.9 / 12.9); B1 12/12 S1024
+// D64 14.9 / 20.5; B2 12/12 S512 D64 13.0 / 13.8; B1 8/2 S512 D128 11.9 /
+// 16.7; B1 8/2 S1024 D128 16.3 / 24.9; B2 8/2 S1024 D128 21.8 / 25.5;
+// B1 8/2 S2048 D128 30.4 / 41.6 (the balanced schedule); B1 32/8 S512 D128
+// 17.4 / 17.4 (two rounds); B4 8/2 S1024 D128, four rounds, 40.1 / 28.4.
+// It takes precedence over the balanced schedule.  ATTN_PREFILL_KS forces
+// it (dense calls without RoPE; the others then take the 4-wave kernel).
+bool prefill_use_ks(int B, int Hq, int S, int D, int causal) {
+  (void)causal;
+  if (D != 64 && D != 128) return false;
+  const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
+  if (sel == ATTN_PREFILL_KS) return true;
+  if (sel != ATTN_PREFILL_AUTO) return false;
+  const long long ks_grid = (long long)B * Hq * ((S + 31) / 32);
+  return ks_grid <= 2LL * device_cu_count();
+}
+
 // Bound of the balanced schedule's wait for a partner's part, in ticks of
 // the 100 MHz real-time counter (-1: the kernel's own rule).
 std::atomic<int> g_split_wait{-1};
@@ -157,8 +181,9 @@ long long prefill_split_pairs(int B, int Hq, int Hkv, int S, int D,
       (Hq / Hkv) % 4 != 0 || B <= 0 || S <= 0)
     return 0;
   const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
-  if (sel == ATTN_PREFILL_W4) return 0;
+  if (sel == ATTN_PREFILL_W4 || sel == ATTN_PREFILL_KS) return 0;
   if (sel == ATTN_PREFILL_AUTO && S < kSplitMinS) return 0;
+  if (prefill_use_ks(B, Hq, S, D, causal)) return 0;   // small launches
   const long long nq = (S + 63) / 64;
   if (nq < 2) return 0;
   if ((long long)B * (Hq / 4) * nq > device_cu_count()) return 0;
@@ -190,6 +215,16 @@ struct Half16Prefill {
             return;
           }
         }
+      }
+      if (use_rope == 0 && cu_seqlens == nullptr && seq_lens == nullptr &&
+          prefill_use_ks(B, Hq, S, D, C)) {
+        hipLaunchKernelGGL((attn::attn_prefill_ks_kernel<T, D, C>),
+                           dim3((unsigned)(B * Hq * ((S + 31) / 32))),
+                           dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B,
+                           Hq, Hkv, S, sl2);
+        return;
+      }
+      if constexpr (D == 128) {
         if (prefill_use_rb(B, Hq, S, D, C)) {
           if ((Hq / Hkv) % 4 == 0) {
             // four query heads of a KV head per workgroup, 64-row tiles
@@ -693,6 +728,7 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
 int attn_decode_auto_splits(int B, int Hkv) { return auto_splits(B, Hkv); }
 
 int attn_prefill_kernel_for(int B, int Hq, int S, int D, int causal) {
+  if (prefill_use_ks(B, Hq, S, D, causal)) return ATTN_PREFILL_KS;
   return prefill_use_rb(B, Hq, S, D, causal) ? ATTN_PREFILL_RB
                                              : ATTN_PREFILL_W4;
 }
@@ -704,7 +740,7 @@ int attn_prefill_split_wait(int ticks) {
 
 int attn_prefill_select(int kernel) {
   if (kernel != ATTN_PREFILL_AUTO && kernel != ATTN_PREFILL_W4 &&
-      kernel != ATTN_PREFILL_RB)
+      kernel != ATTN_PREFILL_RB && kernel != ATTN_PREFILL_KS)
     return ATTN_ERR_SHAPE;
   return g_prefill_kernel.exchange(kernel);
 }

@@ -270,26 +270,32 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
 /*
  * Which kernel the 16-bit prefill entry points (attn_prefill*, bf16 and
  * fp16) launch, process-wide: ATTN_PREFILL_AUTO picks from the shape (the
- * register-blocked kernel for head dim 128 and large launches, the 4-wave
- * kernel otherwise); ATTN_PREFILL_W4 and ATTN_PREFILL_RB force one (RB
- * applies to head dim 128 only; D = 64 always uses W4).  Both compute the
- * same function; they differ in rounding order only.  For tuning and
- * testing.  Returns the previous setting, or ATTN_ERR_SHAPE for another
- * value (the setting is then unchanged).  Launches already issued keep
- * their kernel; calls racing with launches on other threads pick either.
+ * key-split kernel for dense launches whose B Hq ceil(S/32) workgroups fit
+ * in one round of the compute units, the register-blocked kernel for head
+ * dim 128 and large launches, the 4-wave kernel otherwise);
+ * ATTN_PREFILL_W4, ATTN_PREFILL_RB and ATTN_PREFILL_KS force one (RB
+ * applies to head dim 128 only, D = 64 then uses W4; KS applies to the
+ * dense entry points without RoPE, the ragged, padded and RoPE entry points
+ * then use W4).  All compute the same function; they differ in rounding
+ * order only.  For tuning and testing.  Returns the previous setting, or
+ * ATTN_ERR_SHAPE for another value (the setting is then unchanged).
+ * Launches already issued keep their kernel; calls racing with launches on
+ * other threads pick either.
  */
 #define ATTN_PREFILL_AUTO 0
 #define ATTN_PREFILL_W4 1
 #define ATTN_PREFILL_RB 2
+#define ATTN_PREFILL_KS 3
 int attn_prefill_select(int kernel);
 
-/* The kernel (ATTN_PREFILL_W4 or ATTN_PREFILL_RB) a 16-bit prefill launch
-   with these sizes would use under the current setting, without a
-   workspace (with one, the balanced schedule runs the RB kernel, four heads
-   per workgroup, wherever attn_prefill_workspace_size is nonzero).  W4 launches
-   B Hq ceil(S/128) workgroups of 256 threads; RB launches B (Hq/4)
-   ceil(S/64) workgroups of 256 threads when Hq/Hkv is a multiple of 4,
-   else B Hq ceil(S/128) of 128 threads. */
+/* The kernel (ATTN_PREFILL_W4, ATTN_PREFILL_RB or ATTN_PREFILL_KS) a dense
+   16-bit prefill launch with these sizes would use under the current
+   setting, without a workspace (with one, the balanced schedule runs the RB
+   kernel, four heads per workgroup, wherever attn_prefill_workspace_size is
+   nonzero).  W4 launches B Hq ceil(S/128) workgroups of 256 threads; RB
+   launches B (Hq/4) ceil(S/64) workgroups of 256 threads when Hq/Hkv is a
+   multiple of 4, else B Hq ceil(S/128) of 128 threads; KS launches
+   B Hq ceil(S/32) workgroups of 256 threads. */
 int attn_prefill_kernel_for(int B, int Hq, int S, int D, int causal);
 
 /*

@@ -29,17 +29,20 @@ def pytest_collection_modifyitems(config, items):
             item.add_marker(skip)
 
 
-@pytest.fixture(params=["w4", "rb", "balanced"])
+@pytest.fixture(params=["w4", "rb", "balanced", "ks"])
 def prefill_kernel(request):
     """Runs a prefill test under each 16-bit prefill kernel and schedule:
-    the 4-wave kernel, the register-blocked one without a workspace, and the
+    the 4-wave kernel, the register-blocked one without a workspace, the
     register-blocked one with a workspace (the balanced causal schedule
-    where it applies, the register-blocked kernel elsewhere).  The
-    register-blocked kernel applies to head dim 128; at D = 64 every run
-    uses the 4-wave kernel.  Restores the automatic choice afterwards."""
+    where it applies, the register-blocked kernel elsewhere), and the
+    key-split kernel (dense calls without RoPE; the others take the 4-wave
+    kernel).  The register-blocked kernel applies to head dim 128; at D = 64
+    the rb runs use the 4-wave kernel.  Restores the automatic choice
+    afterwards."""
     from causal_attention_amd import attn
     prev = attn.prefill_select({"w4": attn.PREFILL_W4, "rb": attn.PREFILL_RB,
-                                "balanced": attn.PREFILL_RB}[request.param])
+                                "balanced": attn.PREFILL_RB,
+                                "ks": attn.PREFILL_KS}[request.param])
     prev_ws = attn.prefill_workspace_policy(request.param == "balanced")
     yield request.param
     attn.prefill_select(prev)

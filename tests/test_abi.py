@@ -69,11 +69,18 @@ def test_status_strings():
 
 def test_prefill_kernel_selection():
     # host-only: the setting and the shape table, no launch
-    W4, RB = attn.PREFILL_W4, attn.PREFILL_RB
+    W4, RB, KS = attn.PREFILL_W4, attn.PREFILL_RB, attn.PREFILL_KS
     assert attn.lib().attn_prefill_select(7) == -2      # rejected, unchanged
     prev = attn.prefill_select(attn.PREFILL_AUTO)
     try:
-        # automatic: head dim 64 always W4; D = 128 by the launch's work
+        # automatic: the key-split kernel when its B Hq ceil(S/32)
+        # workgroups fit in two rounds (256 compute units without a device)
+        assert attn.prefill_kernel_for(1, 12, 512, 64) == KS
+        assert attn.prefill_kernel_for(1, 8, 1024, 128) == KS
+        assert attn.prefill_kernel_for(1, 8, 2048, 128) == KS
+        assert attn.prefill_kernel_for(1, 12, 2048, 64) == W4
+        assert attn.prefill_workgroups(1, 12, 12, 512, 64) == (KS, 192, 256)
+        # otherwise head dim 64 always W4; D = 128 by the launch's work
         assert attn.prefill_kernel_for(1, 8, 32768, 64) == W4
         assert attn.prefill_kernel_for(1, 8, 32768, 128) == RB
         assert attn.prefill_kernel_for(4, 8, 2048, 128) == W4
@@ -104,13 +111,28 @@ def test_prefill_kernel_selection():
                 RB, 4 * 2 * 32, 256)
             assert not attn.prefill_balanced(4, 8, 2, 2048, 128,
                                              causal=False)
+            # the key-split kernel takes precedence for small launches
+            assert not attn.prefill_balanced(1, 8, 2, 2048, 128)
+            assert attn.prefill_workgroups(1, 8, 2, 2048, 128) == (
+                KS, 8 * 64, 256)
+            assert attn.prefill_balanced(1, 8, 2, 4096, 128)
             attn.prefill_workspace_policy(False)
             assert attn.prefill_workgroups(4, 8, 2, 2048, 128) == (
                 W4, 4 * 8 * 16, 256)
         finally:
             attn.prefill_workspace_policy(prev_ws)
+        # forced key-split: any size
+        attn.prefill_select(KS)
+        assert attn.prefill_kernel_for(1, 8, 32768, 128) == KS
+        assert attn.prefill_workgroups(2, 8, 2, 1000, 64) == (KS, 2 * 8 * 32,
+                                                             256)
+        prev_ws = attn.prefill_workspace_policy(True)
+        try:
+            assert not attn.prefill_balanced(4, 8, 2, 2048, 128)
+        finally:
+            attn.prefill_workspace_policy(prev_ws)
         with pytest.raises(ValueError):
-            attn.prefill_select(3)
+            attn.prefill_select(4)
     finally:
         attn.prefill_select(prev)
 
@@ -169,7 +191,10 @@ def test_prefill_workspace_size():
         # automatic choice: from S = 2048 on only
         assert ws(2, 8, 2, 300, 128) == 0
         assert ws(1, 8, 2, 2047, 128) == 0
-        assert ws(1, 8, 2, 2048, 128) == 4096 + 32 * 4 * 33 * 64 * 16
+        # B1 S2048 is small enough for the key-split kernel, which takes
+        # precedence; S4096 is not
+        assert ws(1, 8, 2, 2048, 128) == 0
+        assert ws(1, 8, 2, 4096, 128) == 4096 + 64 * 4 * 33 * 64 * 16
         assert ws(4, 8, 2, 2048, 128, causal=False) == 0
         assert ws(4, 8, 2, 2048, 64) == 0          # head dim 64
         assert ws(4, 8, 4, 2048, 128) == 0         # group size 2
@@ -181,7 +206,10 @@ def test_prefill_workspace_size():
         attn.prefill_select(attn.PREFILL_RB)
         assert ws(2, 8, 2, 300, 128) == 4096 + 2 * 2 * 2 * 4 * 33 * 64 * 16
         assert ws(1, 8, 2, 64, 128) == 0           # still one query tile
+        assert ws(1, 8, 2, 2048, 128) == 4096 + 32 * 4 * 33 * 64 * 16
         attn.prefill_select(attn.PREFILL_W4)
+        assert ws(4, 8, 2, 2048, 128) == 0
+        attn.prefill_select(attn.PREFILL_KS)
         assert ws(4, 8, 2, 2048, 128) == 0
     finally:
         attn.prefill_select(prev)

@@ -641,14 +641,29 @@ def test_prefill_padded_matches_oracle(B, Hq, Hkv, S, D, lens, causal):
 
 
 def dense_one_range(q, k, v):
-    """Dense prefill without a workspace: every query tile in one workgroup
-    over its whole key range, the launch shape the padded and ragged entry
-    points share (the balanced schedule merges two key ranges of some tiles
-    and so rounds differently)."""
+    """Dense prefill without a workspace and without the key-split kernel:
+    every query tile in one workgroup over its whole key range, the launch
+    shape the padded and ragged entry points share (the balanced schedule
+    and the key-split kernel merge key ranges and so round differently).
+    The kernel is the one those entry points take under the current
+    setting: under ATTN_PREFILL_KS the 4-wave kernel, under the automatic
+    choice its shape table without the key-split rule (the register-blocked
+    kernel for head dim 128 from 4e8 score elements on)."""
     prev = attn.prefill_workspace_policy(False)
+    sel = attn.prefill_select(attn.PREFILL_AUTO)
+    B, Hq, S, D = q.shape
+    if sel == attn.PREFILL_KS:
+        force = attn.PREFILL_W4
+    elif sel == attn.PREFILL_AUTO:
+        big = D == 128 and B * Hq * S * (S + 1) / 2 >= 4e8
+        force = attn.PREFILL_RB if big else attn.PREFILL_W4
+    else:
+        force = sel
+    attn.prefill_select(force)
     try:
         return attn.attn_prefill(q, k, v)
     finally:
+        attn.prefill_select(sel)
         attn.prefill_workspace_policy(prev)
 
 
