@@ -317,6 +317,27 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
         attn.prefill_workspace_policy(prev_ws)
     out["prefill_residual_rmsnorm"]["extra_bytes"] = int(
         2 * res.numel() * res.element_size() + wgt.numel() * 2)
+
+    # the same at a size the register-blocked kernel takes (B1, S16384),
+    # beside the plain prefill on that kernel (no workspace)
+    Sl = 16384
+    ql, kl, vl = (t.to(dev) for t in inputs.prefill_inputs(
+        1, wp.Hq, wp.Hkv, Sl, wp.D, "bf16", 1.0, wp.seed))
+    resl, wgtl = (t.to(dev) for t in inputs.residual_inputs(
+        1, wp.Hq, Sl, wp.D, "bf16", 1.0, wp.seed))
+    ol, oln = torch.empty_like(ql), torch.empty_like(ql)
+    lflops = prefill_flops(1, wp.Hq, Sl, wp.D)
+    out["prefill_residual_rmsnorm_s16384"] = tf(lflops, timed(
+        lambda: attn.attn_prefill_residual_rmsnorm(ql, kl, vl, resl, wgtl,
+                                                   out=ol, with_lse=False)))
+    prev_ws = attn.prefill_workspace_policy(False)
+    try:
+        out["prefill_plain_s16384"] = tf(lflops, timed(
+            lambda: attn.attn_prefill(ql, kl, vl, out=oln, with_lse=False)))
+    finally:
+        attn.prefill_workspace_policy(prev_ws)
+    out["prefill_residual_rmsnorm_s16384"]["kernel"] = \
+        attn.PREFILL_KERNEL_NAMES[attn.prefill_kernel_for(1, wp.Hq, Sl, wp.D)]
     return out
 
 

@@ -211,7 +211,8 @@ struct Half16Prefill {
                                dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq4, ncu, 0, rope, nullptr, nullptr,
                                split_ws,
-                               g_split_wait.load(std::memory_order_relaxed));
+                               g_split_wait.load(std::memory_order_relaxed),
+                               attn::RmsEpilogue<T>{});
             return;
           }
         }
@@ -221,7 +222,7 @@ struct Half16Prefill {
         hipLaunchKernelGGL((attn::attn_prefill_ks_kernel<T, D, C>),
                            dim3((unsigned)(B * Hq * ((S + 31) / 32))),
                            dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B,
-                           Hq, Hkv, S, sl2);
+                           Hq, Hkv, S, sl2, attn::RmsEpilogue<T>{});
         return;
       }
       if constexpr (D == 128) {
@@ -233,12 +234,12 @@ struct Half16Prefill {
                                dim3((unsigned)(B * (Hq / 4) * nq4)),
                                dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq4, ncu, use_rope, rope, cu_seqlens,
-                               seq_lens, nullptr, -1);
+                               seq_lens, nullptr, -1, attn::RmsEpilogue<T>{});
           } else {
             hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 1>), g,
                                dim3(128), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq, ncu, use_rope, rope, cu_seqlens,
-                               seq_lens, nullptr, -1);
+                               seq_lens, nullptr, -1, attn::RmsEpilogue<T>{});
           }
           return;
         }
@@ -374,8 +375,9 @@ int prefill16(const void* q, const void* k, const void* v, void* o,
       split_ws);
 }
 
-// Prefill with the residual-add + RMSNorm epilogue: the 4-wave kernel with
-// its RMS flag, dense [B, H, S, D] tensors, any shape the prefill accepts.
+// Prefill with the residual-add + RMSNorm epilogue: the plain dense
+// prefill's kernel (key-split, register-blocked or 4-wave, without the
+// balanced schedule) with its RMS flag, any shape the prefill accepts.
 template <typename T>
 int prefill16_rms(const void* q, const void* k, const void* v,
                   void* residual, const void* weight, void* out, float* lse,
@@ -401,14 +403,52 @@ int prefill16_rms(const void* q, const void* k, const void* v,
   const attn::RmsEpilogue<T> rms{static_cast<T*>(residual),
                                  static_cast<const T*>(weight), eps};
   const attn::RopeRates rope{};
+  // the kernel table of the plain dense prefill, without the balanced
+  // schedule (no workspace here)
+  const bool ks = prefill_use_ks(B, Hq, S, D, causal);
+  const bool rb = !ks && prefill_use_rb(B, Hq, S, D, causal);
+  const dim3 gks((unsigned)(B * Hq * ((S + 31) / 32)));
 #define ATTN_RMS_LAUNCH(DD, CC)                                               \
-  hipLaunchKernelGGL((attn::attn_prefill_kernel<T, DD, CC, true>), g, b, 0,  \
-                     hs, qt, kt, vt, ot, lse, B, Hq, Hkv, S, sl2, nq, ncu, 0, \
-                     rope, nullptr, nullptr, rms)
+  if (ks)                                                                     \
+    hipLaunchKernelGGL((attn::attn_prefill_ks_kernel<T, DD, CC, true>), gks, \
+                       b, 0, hs, qt, kt, vt, ot, lse, B, Hq, Hkv, S, sl2,     \
+                       rms);                                                  \
+  else                                                                        \
+    hipLaunchKernelGGL((attn::attn_prefill_kernel<T, DD, CC, true>), g, b, 0,\
+                       hs, qt, kt, vt, ot, lse, B, Hq, Hkv, S, sl2, nq, ncu,  \
+                       0, rope, nullptr, nullptr, rms)
   if (D == 64) {
-    if (causal) ATTN_RMS_LAUNCH(64, true); else ATTN_RMS_LAUNCH(64, false);
+    if (causal) { ATTN_RMS_LAUNCH(64, true); } else { ATTN_RMS_LAUNCH(64, false); }
+  } else if (rb && (Hq / Hkv) % 4 == 0) {
+    const int nq4 = (S + 63) / 64;
+    const dim3 g4((unsigned)(B * (Hq / 4) * nq4));
+    if (causal)
+      hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, 128, true, 4, false,
+                                                       true>),
+                         g4, dim3(256), 0, hs, qt, kt, vt, ot, lse, B, Hq,
+                         Hkv, S, sl2, nq4, ncu, 0, rope, nullptr, nullptr,
+                         nullptr, -1, rms);
+    else
+      hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, 128, false, 4,
+                                                       false, true>),
+                         g4, dim3(256), 0, hs, qt, kt, vt, ot, lse, B, Hq,
+                         Hkv, S, sl2, nq4, ncu, 0, rope, nullptr, nullptr,
+                         nullptr, -1, rms);
+  } else if (rb) {
+    if (causal)
+      hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, 128, true, 1, false,
+                                                       true>),
+                         g, dim3(128), 0, hs, qt, kt, vt, ot, lse, B, Hq, Hkv,
+                         S, sl2, nq, ncu, 0, rope, nullptr, nullptr, nullptr,
+                         -1, rms);
+    else
+      hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, 128, false, 1,
+                                                       false, true>),
+                         g, dim3(128), 0, hs, qt, kt, vt, ot, lse, B, Hq, Hkv,
+                         S, sl2, nq, ncu, 0, rope, nullptr, nullptr, nullptr,
+                         -1, rms);
   } else {
-    if (causal) ATTN_RMS_LAUNCH(128, true); else ATTN_RMS_LAUNCH(128, false);
+    if (causal) { ATTN_RMS_LAUNCH(128, true); } else { ATTN_RMS_LAUNCH(128, false); }
   }
 #undef ATTN_RMS_LAUNCH
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

@@ -340,6 +340,64 @@ struct RmsEpilogue {
   float eps;
 };
 
+// The epilogue of one query row in the transposed-output layout shared by
+// the 16-bit kernels: the lane holding the row (hh = 0) and its partner in
+// the other wave half (hh = 1) hold its D = 32 NDB values between them,
+// element 4a + e of accumulator db being dim 32db + 8a + 4hh + e.  acc holds
+// the unnormalised output, inv = 1 / l.  Both lanes must call it (the
+// squared sums are exchanged); a row past the end (live false) only skips
+// memory.  Writes y to O's row and x to the residual's row.
+template <typename T, int NDB>
+__device__ __forceinline__ void rms_epilogue_row(f32x16 (&acc)[NDB],
+                                                 float inv, bool live,
+                                                 size_t row, int hh,
+                                                 T* __restrict__ O,
+                                                 const RmsEpilogue<T>& rms) {
+  using E = Elem16<T>;
+  typedef T t4 __attribute__((ext_vector_type(4)));
+  constexpr int D = NDB * 32;
+  T* xrow = rms.resid + row * D;
+  float ss = 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      u32x2 rr = u32x2{};
+      if (live)
+        rr = *reinterpret_cast<const u32x2*>(xrow + db * 32 + 8 * a + 4 * hh);
+      const t4 r4 = __builtin_bit_cast(t4, rr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[db][4 * a + e] * inv + (float)r4[e];
+        acc[db][4 * a + e] = x;
+        ss = fmaf(x, x, ss);
+      }
+    }
+  ss += __shfl_xor(ss, 32, 64);
+  const float rs = 1.f / sqrtf(ss * (1.f / D) + rms.eps);
+  if (!live) return;
+  T* orow = O + row * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int col = db * 32 + 8 * a + 4 * hh;
+      const t4 w4 = __builtin_bit_cast(t4,
+                                       *reinterpret_cast<const u32x2*>(
+                                           rms.w + col));
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e];
+      u32x2 py, px;
+      py[0] = E::pack2(x[0] * rs * (float)w4[0], x[1] * rs * (float)w4[1]);
+      py[1] = E::pack2(x[2] * rs * (float)w4[2], x[3] * rs * (float)w4[3]);
+      px[0] = E::pack2(x[0], x[1]);
+      px[1] = E::pack2(x[2], x[3]);
+      *reinterpret_cast<u32x2*>(orow + col) = py;
+      *reinterpret_cast<u32x2*>(xrow + col) = px;
+    }
+}
+
 template <typename T, int D, bool CAUSAL, bool RMS = false>
 __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
@@ -595,56 +653,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void attn_prefill_kernel(
   // Epilogue: O = acc / l (input type, RNE) and LSE = (m_ref + log2 l) * ln 2.
   const float l_tot = l_i + swap_halves(l_i);
   if constexpr (RMS) {
-    // Lane `query` (hh = 0) and its partner in the other half (hh = 1) hold
-    // the row's D values between them: dims 32db + 8a + 4hh + 0..3.  Both
-    // run the exchange of the squared sums; rows past S only skip memory.
-    typedef T t4 __attribute__((ext_vector_type(4)));
     const bool live = query < S;
-    const float inv = 1.f / l_tot;
-    const size_t row = q_row0 + (live ? query : 0);
-    T* xrow = rms.resid + row * D;
-    float ss = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 rr = u32x2{};
-        if (live)
-          rr = *reinterpret_cast<const u32x2*>(xrow + db * 32 + 8 * a +
-                                               4 * hh);
-        const t4 r4 = __builtin_bit_cast(t4, rr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = oacc[db][4 * a + e] * inv + (float)r4[e];
-          oacc[db][4 * a + e] = x;
-          ss = fmaf(x, x, ss);
-        }
-      }
-    ss += swap_halves(ss);
-    const float rs = 1.f / sqrtf(ss * (1.f / D) + rms.eps);
-    if (live) {
-      T* orow = O + row * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int col = db * 32 + 8 * a + 4 * hh;
-          const u32x2 wr = *reinterpret_cast<const u32x2*>(rms.w + col);
-          const t4 w4 = __builtin_bit_cast(t4, wr);
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * a + e];
-          u32x2 py, px;
-          py[0] = E::pack2(x[0] * rs * (float)w4[0], x[1] * rs * (float)w4[1]);
-          py[1] = E::pack2(x[2] * rs * (float)w4[2], x[3] * rs * (float)w4[3]);
-          px[0] = E::pack2(x[0], x[1]);
-          px[1] = E::pack2(x[2], x[3]);
-          *reinterpret_cast<u32x2*>(orow + col) = py;
-          *reinterpret_cast<u32x2*>(xrow + col) = px;
-        }
-      if (LSE != nullptr && hh == 0)
-        LSE[q_row0 + query] = (m_i + fast_log2(l_tot)) * kLn2;
-    }
+    rms_epilogue_row<T, NDB>(oacc, 1.f / l_tot, live,
+                             q_row0 + (live ? query : 0), hh, O, rms);
+    if (live && LSE != nullptr && hh == 0)
+      LSE[q_row0 + query] = (m_i + fast_log2(l_tot)) * kLn2;
   } else if (query < S) {
     const float inv = 1.f / l_tot;
     T* orow = O + (q_row0 + query) * D;
@@ -886,7 +899,8 @@ __host__ __device__ __forceinline__ size_t rb_split_bytes(long long np) {
 // query tiles, one workgroup per compute unit): every K / V tile loaded
 // into LDS feeds 256 query rows instead of 128, and all waves share one
 // causal diagonal.
-template <typename T, int D, bool CAUSAL, int GQ, bool SPLIT = false>
+template <typename T, int D, bool CAUSAL, int GQ, bool SPLIT = false,
+          bool RMS = false>
 __global__ __launch_bounds__(GQ == 4 ? 256 : 128, GQ == 4 ? 1 : 2)
 void attn_prefill_rb_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
@@ -894,8 +908,9 @@ void attn_prefill_rb_kernel(
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S_all,
     float scale_log2, int n_qtiles, int n_cu, int use_rope, RopeRates rope,
     const int* __restrict__ cu_seqlens, const int* __restrict__ seq_lens,
-    void* __restrict__ ws, int wait_ticks) {
+    void* __restrict__ ws, int wait_ticks, RmsEpilogue<T> rms) {
   static_assert(D == 128, "64 rows per wave at head dim 128");
+  static_assert(!(RMS && SPLIT), "the fused epilogue has no split form");
   static_assert(GQ == 1 || GQ == 4, "heads per workgroup");
   static_assert(!SPLIT || (GQ == 4 && CAUSAL), "balanced causal schedule");
   constexpr int WAVES = GQ == 4 ? 4 : 2;
@@ -1535,6 +1550,15 @@ void attn_prefill_rb_kernel(
   for (int rb = 0; rb < 2; ++rb) {
     const int query = wq0 + 32 * rb + r;
     const float l_tot = l_i[rb] + swap_halves(l_i[rb]);
+    if constexpr (RMS) {
+      // residual add + RMSNorm (dense launches only)
+      const bool live = query < S;
+      rms_epilogue_row<T, NDB>(oacc[rb], 1.f / l_tot, live,
+                               q_row0 + (live ? query : 0), hh, O, rms);
+      if (live && LSE != nullptr && hh == 0)
+        LSE[q_row0 + query] = (m_ref[rb] + fast_log2(l_tot)) * kLn2;
+      continue;
+    }
     if (query < S) {
       const float inv = 1.f / l_tot;
       T* orow = O + (q_row0 + query) * D;

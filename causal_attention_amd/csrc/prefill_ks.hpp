@@ -33,12 +33,12 @@ struct KsLayout {
   static_assert(NLI == 8 && TILE * 2 == 8192, "8 KB tiles, 8 loads");
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool RMS = false>
 __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_ks_kernel(
     const T* __restrict__ Q, const T* __restrict__ K,
     const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int B, int Hq, int Hkv, int S,
-    float scale_log2) {
+    float scale_log2, RmsEpilogue<T> rms) {
   using L = KsLayout<D>;
   constexpr int BN = L::BN, NKB = L::NKB, CPR = L::CPR, RPI = L::RPI;
   constexpr int TILE = L::TILE;
@@ -206,6 +206,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_ks_kernel(
     } else {
       wait_vmem();
     }
+    // no LDS read of this tile may be placed above the wait (there is no
+    // barrier here to order them)
+    asm volatile("" ::: "memory");
     const T* Kt = ring + (i & 1) * 2 * TILE;
     tile_body(jt >= n_full, jt * BN, Kt, Kt + TILE);
   }
@@ -253,7 +256,14 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_ks_kernel(
       oacc[db][e] = o;
     }
   const float l_tot = l + swap_halves(l);
-  if (query < S) {
+  if constexpr (RMS) {
+    // residual add + RMSNorm of the merged row
+    const bool live = query < S;
+    rms_epilogue_row<T, NDB>(oacc, 1.f / l_tot, live,
+                             q_row0 + (live ? query : 0), hh, O, rms);
+    if (live && LSE != nullptr && hh == 0)
+      LSE[q_row0 + query] = (M + fast_log2(l_tot)) * kLn2;
+  } else if (query < S) {
     const float inv = 1.f / l_tot;
     T* orow = O + (q_row0 + query) * D;
 #pragma unroll

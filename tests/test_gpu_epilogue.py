@@ -1,7 +1,8 @@
 """GPU parity of the fused residual-add + RMSNorm prefill epilogue.
 
 attn_prefill_residual_rmsnorm (bf16) and its fp16 sibling, through the C
-ABI, against the fp64 oracle (oracle.prefill_residual_rmsnorm): the
+ABI, under each prefill kernel that carries the epilogue (4-wave,
+register-blocked, key-split), against the fp64 oracle (oracle.prefill_residual_rmsnorm): the
 "triton-optimization" page's fused RMSNorm with residual (section 3.2)
 applied to each head row of the attention output, the extension named by
 the attention-fusion page, section 6.3.
@@ -71,8 +72,42 @@ def check(B, Hq, Hkv, S, D, dtype, causal, eps=1e-6, seed=0):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("S", [1, 63, 200, 513])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_residual_rmsnorm_shapes(dtype, D, causal, S):
     check(2, 8, 2, S, D, dtype, causal, seed=S)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 8)])
+def test_residual_rmsnorm_long_rows_sampled(Hq, Hkv):
+    """A launch large enough for the register-blocked kernel under the
+    automatic choice (four query heads per workgroup with 8/2 heads, one
+    with 8/8), checked on 64 seeded rows per head: the oracle's attention
+    rows followed by its epilogue on those rows."""
+    from causal_attention_amd import attn as A
+    B, S, D = 1, 16384, 128
+    assert A.prefill_kernel_for(B, Hq, S, D) == A.PREFILL_RB
+    say(f"[prefill+rmsnorm sampled] B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, D, "bf16", 1.0, 9)
+    res, w = inputs.residual_inputs(B, Hq, S, D, "bf16", 1.0, 9)
+    res_d = res.to(DEV)
+    out, lse = attn.attn_prefill_residual_rmsnorm(
+        q.to(DEV), k.to(DEV), v.to(DEV), res_d, w.to(DEV))
+    torch.cuda.synchronize()
+    rows = inputs.sampled_rows(Hq, S, 64)
+    ro, rl = oracle.prefill_rows(np64(q), np64(k), np64(v),
+                                 1 / math.sqrt(D), True, rows)
+    rr = np.stack([np64(res[:, h, rows[h]]) for h in range(Hq)], axis=1)
+    ry, rx = oracle.residual_rmsnorm(ro, rr, np64(w), 1e-6)
+    gy = np.stack([np64(out[:, h, rows[h]]) for h in range(Hq)], axis=1)
+    gx = np.stack([np64(res_d[:, h, rows[h]]) for h in range(Hq)], axis=1)
+    gl = np.stack([lse[:, h, rows[h]].cpu().numpy() for h in range(Hq)],
+                  axis=1)
+    atol, rtol = TOL["bf16"]
+    ey = (np.abs(gy - ry) / (atol + rtol * np.abs(ry))).max()
+    ex = (np.abs(gx - rx) / (atol + rtol * np.abs(rx))).max()
+    el = np.abs(gl - rl).max()
+    say(f"   worst/bound y {ey:.3f} x {ex:.3f} max|dLSE|={el:.3e}")
+    assert ey <= 1.0 and ex <= 1.0 and el <= 1e-3
 
 
 def test_residual_rmsnorm_c2_shape():
@@ -88,19 +123,20 @@ def test_residual_rmsnorm_eps(eps):
     check(1, 4, 1, 130, 128, "bf16", True, eps=eps, seed=7)
 
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_residual_rmsnorm_attention_part_equals_plain_prefill():
     """With a zero residual and unit weight, out is RMSNorm(o) for the
-    attention row o; LSE is the plain prefill's, bit for bit, and the
-    residual buffer receives o itself (rounded), within one rounding of the
-    plain prefill's output."""
+    attention row o; under each kernel, LSE is the plain prefill's (the same
+    kernel, no workspace) bit for bit, and the residual buffer receives o
+    itself, rounded the same way."""
     B, Hq, Hkv, S, D = 1, 8, 2, 300, 128
     q, k, v = [t.to(DEV) for t in inputs.prefill_inputs(B, Hq, Hkv, S, D,
                                                          "bf16", 1.0, 3)]
-    prev = attn.prefill_select(attn.PREFILL_W4)
+    prev_ws = attn.prefill_workspace_policy(False)
     try:
         o, lse = attn.attn_prefill(q, k, v, causal=True)
     finally:
-        attn.prefill_select(prev)
+        attn.prefill_workspace_policy(prev_ws)
     res = torch.zeros_like(q)
     w = torch.ones(D, dtype=torch.bfloat16, device=DEV)
     y, lse2 = attn.attn_prefill_residual_rmsnorm(q, k, v, res, w, eps=0.0)
