@@ -55,25 +55,33 @@ constexpr int kDecodeBlock = 32;                  // keys per block
 
 // T blocks cut into P equal contiguous ranges: range i starts at
 // floor(i*T/P) = q*i + floor(r*i/P) with T = q*P + r (r*i < P*P, so the
-// second division is 32-bit).
+// second division is 32-bit).  The two 64-bit quotients below (q, and the
+// range holding a block) come from one double-precision division each,
+// corrected by one step: for T < 2^40 and P <= 4096 the numerators are
+// exact doubles and the rounded quotient is within one of the true one.
+// (A binary search over lo() cost about a microsecond per segment end,
+// on one lane, in the middle of a range's stream.)
 struct Ranges {
-  long long q;
+  long long T, q;
   int r, P;
-  __device__ __forceinline__ Ranges(long long T, int P_) : P(P_) {
-    q = T / P_;
-    r = (int)(T - q * P_);
+  __host__ __device__ __forceinline__ Ranges(long long T_, int P_)
+      : T(T_), P(P_) {
+    q = (long long)((double)T_ / (double)P_);
+    if (q * P_ > T_) --q;
+    else if ((q + 1) * P_ <= T_) ++q;
+    r = (int)(T_ - q * P_);
   }
-  __device__ __forceinline__ long long lo(int i) const {
+  __host__ __device__ __forceinline__ long long lo(int i) const {
     return q * i + (unsigned)(r * i) / (unsigned)P;
   }
-  // The range holding block x (0 <= x < T): the largest i with lo(i) <= x.
-  __device__ __forceinline__ int owner(long long x) const {
-    int a = 0, b = P - 1;
-    while (a < b) {
-      const int mid = (a + b + 1) >> 1;
-      if (lo(mid) <= x) a = mid; else b = mid - 1;
-    }
-    return a;
+  // The range holding block x (0 <= x < T): the largest i with lo(i) <= x,
+  // which is floor(((x + 1) P - 1) / T).
+  __host__ __device__ __forceinline__ int owner(long long x) const {
+    const long long num = (x + 1) * P - 1;
+    long long i = (long long)((double)num / (double)T);
+    if (i * T > num) --i;
+    else if ((i + 1) * T <= num) ++i;
+    return (int)i;
   }
 };
 
@@ -244,7 +252,9 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(
       lb = __builtin_ctzll(hit);
       const long long sb = lane_i64(ch.bx, lb) * Hkv;
       const int nbb = __builtin_amdgcn_readlane(ch.nb, lb);
-      g0 = (int)((lo - sb) / nbb);
+      const long long into = lo - sb;    // < Hkv * nbb
+      g0 = into <= 0x7fffffffLL ? (int)((unsigned)into / (unsigned)nbb)
+                                : (int)(into / nbb);
       break;
     }
     ch = load_chunk(seqlens, B, cap, ch.base + 64, ch.kend, ch.bend, lane);

@@ -327,7 +327,7 @@ __device__ __forceinline__ void lds_buffer_load16_at(const u32x4& rsrc,
 // s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Residual add and RMSNorm fused into the 4-wave kernel's epilogue (the
+// Residual add and RMSNorm fused into the 16-bit kernels' epilogue (the
 // fused RMSNorm-with-residual of the "triton-optimization" page, section
 // 3.2, applied to each query row of one head, the next extension named by
 // section 6.3 of the attention-fusion page): x = o + residual with o the

@@ -234,8 +234,9 @@ int attn_prefill_padded_f16(const void* q, const void* k, const void* v,
  *   weight : [D] bf16    lse : [B, Hq, S] fp32 (the attention's), or NULL
  *   eps    : >= 0 and finite (the pages' default is 1e-6; with eps = 0 an
  *            all-zero row x gives NaN)
- * The row normalised is one head's D values.  Always the 4-wave prefill
- * kernel; other arguments as attn_prefill.  Errors as attn_prefill, plus:
+ * The row normalised is one head's D values.  The kernel is the one
+ * attn_prefill would take without a workspace (attn_prefill_kernel_for);
+ * other arguments as attn_prefill.  Errors as attn_prefill, plus:
  * residual or weight NULL -> ATTN_ERR_NULL; either not 16-byte aligned ->
  * ATTN_ERR_ALIGN; eps negative or not finite -> ATTN_ERR_SCALE; residual ==
  * out -> ATTN_ERR_SHAPE.
