@@ -80,7 +80,9 @@ def decode_bytes(seqlens, Hq, Hkv, D, elt=2):
 
 KERNEL_SOURCES = ("causal_attention_amd/csrc/common.hpp",
                   "causal_attention_amd/csrc/prefill.hpp",
+                  "causal_attention_amd/csrc/prefill_ks.hpp",
                   "causal_attention_amd/csrc/decode.hpp",
+                  "causal_attention_amd/csrc/kvcache.hpp",
                   "causal_attention_amd/csrc/attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -207,7 +209,7 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
     (the same FLOP and byte counts as the main line) against the same
     peaks (fp16 dense MFMA peak = bf16's)."""
     def timed(fn):
-        for _ in range(3):
+        for _ in range(10):
             fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
