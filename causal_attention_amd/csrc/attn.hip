@@ -152,10 +152,11 @@ bool prefill_use_rb(int B, int Hq, int S, int D, int causal) {
 bool prefill_use_ks(int B, int Hq, int S, int D, int causal) {
   (void)causal;
   if (D != 64 && D != 128) return false;
-  const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
-  if (sel == ATTN_PREFILL_KS) return true;
-  if (sel != ATTN_PREFILL_AUTO) return false;
   const long long ks_grid = (long long)B * Hq * ((S + 31) / 32);
+  const int sel = g_prefill_kernel.load(std::memory_order_relaxed);
+  // forced: wherever the grid is addressable (else the 4-wave kernel)
+  if (sel == ATTN_PREFILL_KS) return ks_grid <= 0x7fffffffLL;
+  if (sel != ATTN_PREFILL_AUTO) return false;
   return ks_grid <= 2LL * device_cu_count();
 }
 
@@ -220,7 +221,7 @@ struct Half16Prefill {
       if (use_rope == 0 && cu_seqlens == nullptr && seq_lens == nullptr &&
           prefill_use_ks(B, Hq, S, D, C)) {
         hipLaunchKernelGGL((attn::attn_prefill_ks_kernel<T, D, C>),
-                           dim3((unsigned)(B * Hq * ((S + 31) / 32))),
+                           dim3((unsigned)((long long)B * Hq * ((S + 31) / 32))),
                            dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B,
                            Hq, Hkv, S, sl2, attn::RmsEpilogue<T>{});
         return;
@@ -407,7 +408,7 @@ int prefill16_rms(const void* q, const void* k, const void* v,
   // schedule (no workspace here)
   const bool ks = prefill_use_ks(B, Hq, S, D, causal);
   const bool rb = !ks && prefill_use_rb(B, Hq, S, D, causal);
-  const dim3 gks((unsigned)(B * Hq * ((S + 31) / 32)));
+  const dim3 gks((unsigned)((long long)B * Hq * ((S + 31) / 32)));
 #define ATTN_RMS_LAUNCH(DD, CC)                                               \
   if (ks)                                                                     \
     hipLaunchKernelGGL((attn::attn_prefill_ks_kernel<T, DD, CC, true>), gks, \

@@ -121,9 +121,10 @@ def test_prefill_kernel_selection():
                 W4, 4 * 8 * 16, 256)
         finally:
             attn.prefill_workspace_policy(prev_ws)
-        # forced key-split: any size
+        # forced key-split: any size whose grid is addressable
         attn.prefill_select(KS)
         assert attn.prefill_kernel_for(1, 8, 32768, 128) == KS
+        assert attn.prefill_kernel_for(64, 128, 1 << 24, 64) == W4
         assert attn.prefill_workgroups(2, 8, 2, 1000, 64) == (KS, 2 * 8 * 32,
                                                              256)
         prev_ws = attn.prefill_workspace_policy(True)
