@@ -250,6 +250,23 @@ def extras(attn, inputs, torch, dev, wp, wd, reps=20):
     dbytes = decode_bytes(sl, wd.Hq, wd.Hkv, wd.D)
     out["decode_f16"] = gb(dbytes, timed(dcall))
 
+    # the same decode at 8x the batch (B = 256, lengths from the same
+    # distribution, about 600 MB of cache): how far the split kernel's
+    # stream goes once the launch's fixed cost is spread over more bytes
+    slb, dqb8, kcb, vcb = inputs.decode_inputs(8 * wd.B, wd.Hq, wd.Hkv, wd.D,
+                                               lmin=wd.lmin, lmax=wd.lmax,
+                                               sigma=wd.sigma, seed=wd.seed)
+    dqb8, kcb, vcb = dqb8.to(dev), kcb.to(dev), vcb.to(dev)
+    sldb = torch.from_numpy(slb).to(dev)
+    wsb = attn.new_decode_workspace(8 * wd.B, wd.Hq, wd.Hkv, wd.D, 0, dev)
+    dob8 = torch.empty_like(dqb8)
+    bcall = attn.prepare_decode(dqb8, kcb, vcb, sldb, dob8, wd.Hkv, wsb)
+    out["decode_b256"] = gb(decode_bytes(slb, wd.Hq, wd.Hkv, wd.D),
+                            timed(bcall))
+    out["decode_b256"]["cache_MB"] = round(
+        2 * kcb.numel() * kcb.element_size() / 1e6, 1)
+    del kcb, vcb
+
     # RoPE: prefill with q rotated on load plus the K rotation pass (timed
     # together; the FLOP count is the attention's), and decode over a padded
     # cache with q rotated in the kernel
