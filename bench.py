@@ -405,6 +405,13 @@ def prefill_launch(attn, w):
     """Kernel name, workgroups and threads per workgroup of one prefill
     launch of workload w."""
     if w.dtype == "f32":
+        if attn.prefill_kernel_for(w.B, w.Hq, w.S, w.D,
+                                   w.causal) == attn.PREFILL_KS:
+            return {"kernel": "attn_prefill_f32_ks_kernel",
+                    "workgroups": w.B * w.Hq * -(-w.S // 32), "threads": 256,
+                    "schedule": ("key split: 32 query rows per workgroup, "
+                                 "its four waves take every fourth key "
+                                 "tile and merge in LDS")}
         return {"kernel": "attn_prefill_f32_kernel",
                 "workgroups": w.B * w.Hq * -(-w.S // 128), "threads": 256}
     kern, wgs, thr = attn.prefill_workgroups(w.B, w.Hq, w.Hkv, w.S, w.D,

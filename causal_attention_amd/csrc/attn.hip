@@ -260,6 +260,13 @@ struct F32Prefill {
                   int /*use_rope*/, const attn::RopeRates& /*rope*/,
                   const int* /*cu_seqlens*/, const int* /*seq_lens*/,
                   void* /*split_ws*/) {
+    if (prefill_use_ks(B, Hq, S, D, C)) {
+      hipLaunchKernelGGL((attn::attn_prefill_f32_ks_kernel<D, C>),
+                         dim3((unsigned)((long long)B * Hq * ((S + 31) / 32))),
+                         dim3(kPrefillThreads), 0, st, q, k, v, o, lse, B, Hq,
+                         Hkv, S, sl2);
+      return;
+    }
     hipLaunchKernelGGL((attn::attn_prefill_f32_kernel<D, C>), g, b, 0, st, q,
                        k, v, o, lse, B, Hq, Hkv, S, sl2, nq, ncu);
   }

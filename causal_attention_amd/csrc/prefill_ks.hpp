@@ -282,3 +282,171 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_ks_kernel(
 }
 
 }  // namespace attn
+
+namespace attn {
+
+// The fp32 sibling of the key-split kernel (the fp32 prefill's steps: one
+// query row per lane of v_mfma_f32_32x32x2_f32, probabilities kept in fp32).
+// Each wave loads its own 32-key tiles through registers into its own LDS
+// rows (padded by 4 floats against bank conflicts), one tile at a time.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPrefillThreads, 1) void attn_prefill_f32_ks_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K,
+    const float* __restrict__ V, float* __restrict__ O,
+    float* __restrict__ LSE, int B, int Hq, int Hkv, int S,
+    float scale_log2) {
+  constexpr int BN = 32, NKB = 1, NDB = D / 32;
+  constexpr int HD = D / 2;                   // contraction elems per half
+  constexpr int STR = D + 4;                  // LDS row stride (floats)
+  constexpr int DCH = D / 4;                  // 16-byte chunks per row
+  constexpr int CH = BN * DCH / 64;           // chunks per lane per tile
+  constexpr int HALF = D == 128 ? 2 : 1;      // K, V staged in turn at 128
+
+  __shared__ __attribute__((aligned(16))) float smem[4 * 2 * BN * STR];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane & 31, hh = lane >> 5;
+
+  const int BH = B * Hq;
+  const int nrb = (S + 31) / 32;
+  const int bid = blockIdx.x;
+  const int rb = CAUSAL ? nrb - 1 - bid / BH : bid / BH;
+  const int b = (bid % BH) / Hq, hq = (bid % BH) % Hq;
+  const int g = hq / (Hq / Hkv);
+  const size_t q_row0 = (size_t)(b * Hq + hq) * S;
+  const float* Qp = Q + q_row0 * D;
+  const float* Kp = K + (size_t)(b * Hkv + g) * S * D;
+  const float* Vp = V + (size_t)(b * Hkv + g) * S * D;
+
+  const int q0 = rb * 32;
+  const int query = q0 + r;
+  const int kv_end = CAUSAL ? min(S, q0 + 32) : S;
+  const int n_kv = (kv_end + BN - 1) / BN;
+
+  float qB[HD];
+#pragma unroll
+  for (int t = 0; t < HD; t += 4) {
+    f32x4 v4 = f32x4{};
+    if (query < S)
+      v4 = *reinterpret_cast<const f32x4*>(Qp + (size_t)query * D + hh * HD +
+                                           t);
+    qB[t] = v4[0]; qB[t + 1] = v4[1]; qB[t + 2] = v4[2]; qB[t + 3] = v4[3];
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_i = -INFINITY, l_i = 0.f;
+
+  float* const Ks = smem + w * 2 * BN * STR;
+  float* const Vs = Ks + BN * STR;
+  // rows past S load as zeros (their scores are masked)
+  auto stage = [&](const float* src, float* dst, int j0) {
+    constexpr int CHH = CH / HALF;
+#pragma unroll
+    for (int h = 0; h < HALF; ++h) {
+      f32x4 reg[CHH];
+#pragma unroll
+      for (int i = 0; i < CHH; ++i) {
+        const int c = lane + (h * CHH + i) * 64;
+        const int row = j0 + c / DCH, col = c % DCH;
+        reg[i] = row < S ? *reinterpret_cast<const f32x4*>(
+                               src + (size_t)row * D + col * 4)
+                         : f32x4{};
+      }
+#pragma unroll
+      for (int i = 0; i < CHH; ++i) {
+        const int c = lane + (h * CHH + i) * 64;
+        *reinterpret_cast<f32x4*>(&dst[(c / DCH) * STR + (c % DCH) * 4]) =
+            reg[i];
+      }
+    }
+  };
+
+  for (int jt = w; jt < n_kv; jt += 4) {
+    const int j0 = jt * BN;
+    stage(Kp, Ks, j0);
+    stage(Vp, Vs, j0);
+    f32x16 sacc[NKB];
+    sacc[0] = f32x16{};
+    const float* krow = &Ks[r * STR + hh * HD];
+#pragma unroll
+    for (int t = 0; t < HD; t += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + t);
+      sacc[0] = mfma_32x32x2_f32(a4[0], qB[t], sacc[0]);
+      sacc[0] = mfma_32x32x2_f32(a4[1], qB[t + 1], sacc[0]);
+      sacc[0] = mfma_32x32x2_f32(a4[2], qB[t + 2], sacc[0]);
+      sacc[0] = mfma_32x32x2_f32(a4[3], qB[t + 3], sacc[0]);
+    }
+    if ((j0 + BN > S) || (CAUSAL && j0 + BN - 1 > q0))
+      apply_mask<NKB, CAUSAL>(sacc, j0, hh, query, S);
+    softmax_step<NKB, NDB>(sacc, scale_log2, m_i, l_i, oacc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hh + (i & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma_32x32x2_f32(Vs[key * STR + db * 32 + r], sacc[0][i],
+                                    oacc[db]);
+    }
+  }
+
+  // Merge through LDS as in the 16-bit key-split kernel.
+  constexpr int NV = NDB * 16 + 2;
+  static_assert(3 * NV * 64 * 4 <= (int)sizeof(smem), "merge area");
+  float* st = smem;
+  __syncthreads();
+  if (w > 0) {
+    float* s0 = st + (size_t)(w - 1) * NV * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s0[(db * 16 + e) * 64] = oacc[db][e];
+    s0[(NV - 2) * 64] = m_i;
+    s0[(NV - 1) * 64] = l_i;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float mw[3], aw[3];
+  float M = m_i;
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    mw[x] = st[((size_t)x * NV + NV - 2) * 64 + lane];
+    M = fmaxf(M, mw[x]);
+  }
+  const float a0 = fast_exp2(m_i - M);
+  float l = a0 * l_i;
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    aw[x] = fast_exp2(mw[x] - M);
+    l = fmaf(aw[x], st[((size_t)x * NV + NV - 1) * 64 + lane], l);
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float o = a0 * oacc[db][e];
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+        o = fmaf(aw[x], st[((size_t)x * NV + db * 16 + e) * 64 + lane], o);
+      oacc[db][e] = o;
+    }
+  const float l_tot = l + swap_halves(l);
+  if (query < S) {
+    const float inv = 1.f / l_tot;
+    float* orow = O + (q_row0 + query) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 o4 = {oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
+                    oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * a + 4 * hh) = o4;
+      }
+    if (LSE != nullptr && hh == 0)
+      LSE[q_row0 + query] = (M + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace attn

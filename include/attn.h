@@ -263,6 +263,9 @@ int attn_prefill_residual_rmsnorm_f16(const void* q, const void* k,
  * Prefill attention, fp32 storage.  Same arguments and layouts as
  * attn_prefill with every tensor fp32.  The probabilities P stay fp32 (the
  * accuracy setting of the attention-fusion page, sections 3.3 and 5.5).
+ * Launches small enough for the key-split rule of attn_prefill_select (or
+ * under ATTN_PREFILL_KS) take the fp32 key-split kernel, the others the
+ * fp32 kernel.
  */
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o,
                      float* lse, int B, int Hq, int Hkv, int S, int D,

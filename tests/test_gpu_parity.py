@@ -86,7 +86,10 @@ def check_prefill(B, Hq, Hkv, S, D, dtype, causal, sigma=1.0, seed=0):
 
 # ------------------------------------------------------------ the workloads
 
+@pytest.mark.usefixtures("prefill_kernel")
 def test_c1_single_head_fp32():
+    # fp32: the fp32 kernel under w4 / rb / balanced, its key-split sibling
+    # under ks
     w = inputs.WORKLOADS["c1_f32_s128"]
     check_prefill(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.causal, w.sigma)
 
@@ -206,6 +209,7 @@ def test_prefill_edge_shapes_bf16(S, D, Hq, Hkv, causal):
 @pytest.mark.parametrize("S", [1, 33, 128, 129, 300])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.usefixtures("prefill_kernel")
 def test_prefill_edge_shapes_f32(S, D, causal):
     check_prefill(1, 4, 2, S, D, "f32", causal, seed=S)
 
