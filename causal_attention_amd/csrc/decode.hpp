@@ -85,6 +85,20 @@ struct Ranges {
   }
 };
 
+// Inclusive prefix sum of x over the 64 lanes of the wave by DPP: shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes (lanes shifted in from
+// outside the row add 0), then lane 15 of rows 0 and 2 added to rows 1 and
+// 3, then lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_scan_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Lane l's value of v as a wave-uniform (scalar) value.
 __device__ __forceinline__ long long lane_i64(long long v, int l) {
   const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffLL), l);
@@ -113,14 +127,23 @@ __device__ __forceinline__ SeqChunk load_chunk(const int* __restrict__ seqlens,
   c.L = (b < B) ? max(seqlens[b], 0) : 0;
   if (cap > 0) c.L = min(c.L, cap);
   c.nb = (c.L + kDecodeBlock - 1) / kDecodeBlock;
-  long long ki = c.L, bi = c.nb;
+  long long ki, bi;
+  if (__ballot(c.L >= (1 << 24)) == 0) {
+    // every length below 2^24, so 64 of them sum below 2^30: 32-bit DPP
+    // scans (this is on every workgroup's path before its first load)
+    ki = wave_scan_add(c.L);
+    bi = wave_scan_add(c.nb);
+  } else {
+    ki = c.L;
+    bi = c.nb;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long kt = __shfl_up(ki, off, 64);
-    const long long bt = __shfl_up(bi, off, 64);
-    if (lane >= off) {
-      ki += kt;
-      bi += bt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long kt = __shfl_up(ki, off, 64);
+      const long long bt = __shfl_up(bi, off, 64);
+      if (lane >= off) {
+        ki += kt;
+        bi += bt;
+      }
     }
   }
   c.kx = k0 + ki - c.L;
