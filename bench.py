@@ -416,13 +416,16 @@ def prefill_launch(attn, w):
                 "workgroups": w.B * w.Hq * -(-w.S // 128), "threads": 256}
     kern, wgs, thr = attn.prefill_workgroups(w.B, w.Hq, w.Hkv, w.S, w.D,
                                              w.causal)
-    balanced = attn.prefill_balanced(w.B, w.Hq, w.Hkv, w.S, w.D, w.causal)
-    if balanced:
+    sched = attn.prefill_schedule(w.B, w.Hq, w.Hkv, w.S, w.D, w.causal)
+    if sched == attn.SCHEDULE_BALANCED:
         schedule = ("balanced: query tiles t and n-1-t paired, each pair's "
                     "key tiles cut between two workgroups")
     elif kern == attn.PREFILL_KS:
         schedule = ("key split: 32 query rows per workgroup, its four waves "
                     "take every fourth key tile and merge in LDS")
+    elif sched == attn.SCHEDULE_QUEUE:
+        schedule = ("tile queue: one workgroup per query tile, each taking "
+                    "the next heaviest tile from a counter in the workspace")
     else:
         schedule = "one workgroup per query tile, heaviest first"
     return {"kernel": attn.PREFILL_KERNEL_NAMES[kern], "workgroups": wgs,

@@ -57,6 +57,8 @@ def lib():
         L.attn_prefill_ws_f16.restype = i
         L.attn_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
         L.attn_prefill_workspace_size.restype = sz
+        L.attn_prefill_schedule.argtypes = [i, i, i, i, i, i]
+        L.attn_prefill_schedule.restype = i
         L.attn_prefill_split_wait.argtypes = [i]
         L.attn_prefill_split_wait.restype = i
         L.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
@@ -185,9 +187,26 @@ _prefill_ws_cache = {}
 
 
 def attn_prefill_workspace_size(B, Hq, Hkv, S, D, causal=True):
-    """Bytes of workspace that enable the balanced causal schedule of a
-    16-bit prefill of these sizes on the current device (0: none)."""
+    """Bytes of workspace that enable the balanced causal schedule or the
+    tile queue of a 16-bit prefill of these sizes on the current device (0:
+    neither applies)."""
     return int(lib().attn_prefill_workspace_size(
+        int(B), int(Hq), int(Hkv), int(S), int(D), int(bool(causal))))
+
+
+SCHEDULE_STATIC, SCHEDULE_BALANCED, SCHEDULE_QUEUE = 0, 1, 2
+SCHEDULE_NAMES = {SCHEDULE_STATIC: "static", SCHEDULE_BALANCED: "balanced",
+                  SCHEDULE_QUEUE: "tile queue"}
+
+
+def prefill_schedule(B, Hq, Hkv, S, D, causal=True):
+    """SCHEDULE_STATIC, SCHEDULE_BALANCED or SCHEDULE_QUEUE: the schedule of
+    a 16-bit ``attn_prefill`` of these sizes under the current kernel and
+    workspace settings (a workspace is passed unless
+    ``prefill_workspace_policy(False)`` is set)."""
+    if not _prefill_ws_on:
+        return SCHEDULE_STATIC
+    return int(lib().attn_prefill_schedule(
         int(B), int(Hq), int(Hkv), int(S), int(D), int(bool(causal))))
 
 
@@ -221,8 +240,8 @@ def new_prefill_workspace(B, Hq, Hkv, S, D, causal=True, device="cuda"):
 def _prefill_workspace(q, B, Hq, Hkv, S, D, causal, workspace=None):
     """The workspace for one 16-bit prefill, or None: the caller's, else one
     zero-filled once and kept per (device, stream), so that calls sharing
-    one never overlap (the library leaves its flag words zero after every
-    call)."""
+    one never overlap (the library leaves its flag words and queue counter
+    zero after every call)."""
     if q.dtype not in _PREFILL_WS_FN:
         return None
     if workspace is not None:
@@ -686,8 +705,7 @@ def prefill_kernel_for(B, Hq, S, D, causal=True):
 def prefill_balanced(B, Hq, Hkv, S, D, causal=True):
     """Whether a 16-bit ``attn_prefill`` of these sizes runs the balanced
     causal schedule (a workspace is passed and the schedule applies)."""
-    return _prefill_ws_on and attn_prefill_workspace_size(
-        B, Hq, Hkv, S, D, causal) > 0
+    return prefill_schedule(B, Hq, Hkv, S, D, causal) == SCHEDULE_BALANCED
 
 
 def prefill_workgroups(B, Hq, Hkv, S, D, causal=True):

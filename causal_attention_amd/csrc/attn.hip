@@ -87,7 +87,8 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
                    int causal, void* stream, int use_rope = 0,
                    const attn::RopeRates& rope = attn::RopeRates{},
                    const int* cu_seqlens = nullptr,
-                   const int* seq_lens = nullptr, void* split_ws = nullptr) {
+                   const int* seq_lens = nullptr, void* split_ws = nullptr,
+                   void* queue_ws = nullptr) {
   const int n_qtiles = (S + kPrefillBM - 1) / kPrefillBM;
   const dim3 grid((unsigned)(B * Hq * n_qtiles));
   const dim3 block(kPrefillThreads);
@@ -98,20 +99,20 @@ int launch_prefill(const T* q, const T* k, const T* v, T* o, float* lse,
     if (causal)
       Launcher<64, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv, S,
                               sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens, split_ws);
+                              cu_seqlens, seq_lens, split_ws, queue_ws);
     else
       Launcher<64, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens, split_ws);
+                              cu_seqlens, seq_lens, split_ws, queue_ws);
   } else {
     if (causal)
       Launcher<128, true>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens, split_ws);
+                              cu_seqlens, seq_lens, split_ws, queue_ws);
     else
       Launcher<128, false>::run(grid, block, st, q, k, v, o, lse, B, Hq, Hkv,
                                 S, sl2, n_qtiles, ncu, use_rope, rope,
-                              cu_seqlens, seq_lens, split_ws);
+                              cu_seqlens, seq_lens, split_ws, queue_ws);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -192,6 +193,24 @@ long long prefill_split_pairs(int B, int Hq, int Hkv, int S, int D,
   return np <= attn::kRBMaxPairs ? np : 0;
 }
 
+// Whether a dense causal 16-bit launch given a workspace runs the
+// register-blocked kernel (four query heads per workgroup) with the tile
+// queue: where that kernel is chosen, the balanced schedule is not, and the
+// launch holds more workgroups than compute units (in one round every
+// workgroup is resident from the start and the queue would only add its
+// atomic round trip).  The queue is the workspace's first word.
+bool prefill_queue_applies(int B, int Hq, int Hkv, int S, int D,
+                           int causal) {
+  if (!causal || D != 128 || B <= 0 || S <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || (Hq / Hkv) % 4 != 0)
+    return false;
+  if (prefill_use_ks(B, Hq, S, D, causal)) return false;
+  if (!prefill_use_rb(B, Hq, S, D, causal)) return false;
+  if ((long long)B * (Hq / 4) * ((S + 63) / 64) <= device_cu_count())
+    return false;
+  return prefill_split_pairs(B, Hq, Hkv, S, D, causal) == 0;
+}
+
 // 16-bit inputs (bf16 or fp16): the MFMA kernels for element type T.
 template <typename T>
 struct Half16Prefill {
@@ -201,7 +220,7 @@ struct Half16Prefill {
                     const T* v, T* o, float* lse, int B, int Hq, int Hkv,
                     int S, float sl2, int nq, int ncu, int use_rope,
                     const attn::RopeRates& rope, const int* cu_seqlens,
-                    const int* seq_lens, void* split_ws) {
+                    const int* seq_lens, void* split_ws, void* queue_ws) {
       if constexpr (D == 128) {
         if constexpr (C) {
           if (split_ws != nullptr) {
@@ -231,11 +250,13 @@ struct Half16Prefill {
           if ((Hq / Hkv) % 4 == 0) {
             // four query heads of a KV head per workgroup, 64-row tiles
             const int nq4 = (S + 63) / 64;
+            // (with a workspace, dense causal launches take their tiles
+            // from the tile queue)
             hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 4>),
                                dim3((unsigned)(B * (Hq / 4) * nq4)),
                                dim3(256), 0, st, q, k, v, o, lse, B, Hq, Hkv,
                                S, sl2, nq4, ncu, use_rope, rope, cu_seqlens,
-                               seq_lens, nullptr, -1, attn::RmsEpilogue<T>{});
+                               seq_lens, queue_ws, -1, attn::RmsEpilogue<T>{});
           } else {
             hipLaunchKernelGGL((attn::attn_prefill_rb_kernel<T, D, C, 1>), g,
                                dim3(128), 0, st, q, k, v, o, lse, B, Hq, Hkv,
@@ -259,7 +280,7 @@ struct F32Prefill {
                   int Hq, int Hkv, int S, float sl2, int nq, int ncu,
                   int /*use_rope*/, const attn::RopeRates& /*rope*/,
                   const int* /*cu_seqlens*/, const int* /*seq_lens*/,
-                  void* /*split_ws*/) {
+                  void* /*split_ws*/, void* /*queue_ws*/) {
     if (prefill_use_ks(B, Hq, S, D, C)) {
       hipLaunchKernelGGL((attn::attn_prefill_f32_ks_kernel<D, C>),
                          dim3((unsigned)((long long)B * Hq * ((S + 31) / 32))),
@@ -367,6 +388,7 @@ int prefill16(const void* q, const void* k, const void* v, void* o,
                                &empty);
   if (st != ATTN_OK || empty) return st;
   void* split_ws = nullptr;
+  void* queue_ws = nullptr;
   if (workspace != nullptr) {
     const long long np = prefill_split_pairs(B, Hq, Hkv, S, D, causal);
     if (np > 0) {
@@ -374,13 +396,18 @@ int prefill16(const void* q, const void* k, const void* v, void* o,
       if (workspace_bytes < attn::rb_split_bytes(np))
         return ATTN_ERR_WORKSPACE;
       split_ws = workspace;
+    } else if (prefill_queue_applies(B, Hq, Hkv, S, D, causal)) {
+      if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+      if (workspace_bytes < (size_t)attn::kRBFlagBytes)
+        return ATTN_ERR_WORKSPACE;
+      queue_ws = workspace;
     }
   }
   return launch_prefill<T, Half16Prefill<T>::template L>(
       static_cast<const T*>(q), static_cast<const T*>(k),
       static_cast<const T*>(v), static_cast<T*>(o), lse, B, Hq, Hkv, S, D,
       scale, causal, stream, 0, attn::RopeRates{}, nullptr, nullptr,
-      split_ws);
+      split_ws, queue_ws);
 }
 
 // Prefill with the residual-add + RMSNorm epilogue: the plain dense
@@ -674,7 +701,20 @@ size_t attn_prefill_workspace_size(int B, int Hq, int Hkv, int S, int D,
                                    int causal) {
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
   const long long np = prefill_split_pairs(B, Hq, Hkv, S, D, causal);
-  return np > 0 ? attn::rb_split_bytes(np) : 0;
+  if (np > 0) return attn::rb_split_bytes(np);
+  return prefill_queue_applies(B, Hq, Hkv, S, D, causal)
+             ? (size_t)attn::kRBFlagBytes
+             : 0;
+}
+
+int attn_prefill_schedule(int B, int Hq, int Hkv, int S, int D, int causal) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return ATTN_SCHEDULE_STATIC;
+  if (prefill_split_pairs(B, Hq, Hkv, S, D, causal) > 0)
+    return ATTN_SCHEDULE_BALANCED;
+  return prefill_queue_applies(B, Hq, Hkv, S, D, causal)
+             ? ATTN_SCHEDULE_QUEUE
+             : ATTN_SCHEDULE_STATIC;
 }
 
 int attn_prefill_ws(const void* q, const void* k, const void* v, void* o,

@@ -23,6 +23,7 @@
 // argument (the scale must be positive).
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "common.hpp"
@@ -92,6 +93,29 @@ constexpr int kPrefillBM = 128;        // query rows per workgroup
 struct TileCoord {
   int b, g, hq, qt;
 };
+
+// Tile queue (register-blocked kernel, causal launches of several rounds,
+// when the caller passes a workspace): each workgroup takes the next work
+// index from a counter in the workspace instead of deriving it from its
+// block index, and the indices run heaviest tile first with no snake.  A
+// compute unit that finishes early, or an XCD that runs faster than the
+// others, then takes the next heaviest tile, so the launch is list-scheduled
+// longest first over the whole GPU.  With hardware dispatch alone every XCD
+// receives a fixed eighth of the blocks: measured on MI355X (B1, 8/2 heads,
+// S = 32768), the XCDs of one KV head ran their tiles 4% slower than the
+// others and finished up to 90 us after them, and the queue took the launch
+// from 1813-1822 to 1720 us.  The counter is zero between launches: the
+// workgroup that draws the launch's last index puts it back to zero (every
+// other workgroup of the launch has drawn by then), and an index is taken
+// modulo the block count, so each launch's draws are a permutation of its
+// blocks.
+__device__ __forceinline__ int queue_take(unsigned* ctr, unsigned nblocks) {
+  const unsigned v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  if (v == nblocks - 1)
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (int)(v % nblocks);
+}
 
 __device__ __forceinline__ TileCoord tile_coord(int bid, int nblocks, int B,
                                                 int Hq, int Hkv, int n_qtiles,
@@ -950,6 +974,13 @@ void attn_prefill_rb_kernel(
     tc.g = sc.g;
     tc.hq = sc.hgrp;
     tc.qt = sc.pair;
+  } else if (ws != nullptr) {
+    // tile queue: dense causal launches only (the host passes no workspace
+    // to the other forms of this kernel)
+    __shared__ int s_idx;
+    if (tid == 0) s_idx = queue_take(static_cast<unsigned*>(ws), gridDim.x);
+    __syncthreads();
+    tc = tile_coord(s_idx, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, INT_MAX);
   } else {
     tc = tile_coord(blockIdx.x, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, n_cu);
   }

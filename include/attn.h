@@ -78,10 +78,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
 
 /*
  * Bytes of device workspace that let attn_prefill_ws (and _ws_f16) run a
- * causal launch with the balanced schedule, 0 where that schedule does not
- * apply.  It applies to causal launches with D = 128, Hq / Hkv a multiple
- * of 4, S > 64, and at most one workgroup of B (Hq/4) ceil(S/64) per
- * compute unit of the current device; under ATTN_PREFILL_AUTO from
+ * causal launch with the balanced schedule or the tile queue (below), 0
+ * where neither applies.  The balanced schedule applies to causal launches
+ * with D = 128, Hq / Hkv a multiple of 4, S > 64, and at most one workgroup
+ * of B (Hq/4) ceil(S/64) per compute unit of the current device; under ATTN_PREFILL_AUTO from
  * S = 2048 on (below that the 4-wave kernel was measured faster), under
  * ATTN_PREFILL_RB for any such S, under ATTN_PREFILL_W4 never.
  * Query tile t needs a number of key tiles growing with t, so when every
@@ -90,21 +90,45 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
  * the pair's key tiles evenly between two workgroups, the second merging
  * the first's part of the longer row range with its own (the merge of key
  * ranges by their maxima and sums, attention-fusion page, section 4.4, with
- * the partial buffer of the Qwen page, section 3.3).  The size depends on
- * the device's compute-unit count: query it with that device current.
+ * the partial buffer of the Qwen page, section 3.3).
+ * The tile queue (4096 bytes) applies to the other causal launches of the
+ * register-blocked kernel with four query heads per workgroup (D = 128,
+ * Hq / Hkv a multiple of 4, the kernel chosen by the table or by
+ * ATTN_PREFILL_RB): launches of more workgroups than compute units, which
+ * run in rounds.  Each workgroup then takes the next query tile, heaviest
+ * first, from a counter in the workspace, so compute units and XCDs that
+ * finish early take more of the work (list scheduling, longest first) where
+ * hardware dispatch alone gives every XCD a fixed share of the tiles.  Both
+ * sizes depend on the device's compute-unit count: query them with that
+ * device current.
  */
 size_t attn_prefill_workspace_size(int B, int Hq, int Hkv, int S, int D,
                                    int causal);
 
+/* Schedules of a 16-bit attn_prefill_ws launch given a workspace. */
+#define ATTN_SCHEDULE_STATIC 0   /* no workspace used */
+#define ATTN_SCHEDULE_BALANCED 1 /* paired tiles, split and merged */
+#define ATTN_SCHEDULE_QUEUE 2    /* tiles taken from the tile queue */
+
+/*
+ * The schedule attn_prefill_ws runs for these sizes when it is given a
+ * workspace of attn_prefill_workspace_size bytes, under the current kernel
+ * setting and device (one of ATTN_SCHEDULE_*; STATIC for invalid sizes).
+ */
+int attn_prefill_schedule(int B, int Hq, int Hkv, int S, int D, int causal);
+
 /*
  * attn_prefill / attn_prefill_f16 with a caller-owned device workspace
- * (16-byte aligned) for the balanced schedule.  workspace NULL, or a launch
- * the schedule does not apply to: the same launch as attn_prefill.  Where
- * it applies, workspace_bytes below attn_prefill_workspace_size is
+ * (16-byte aligned) for the balanced schedule or the tile queue.  workspace
+ * NULL, or a launch neither applies to: the same launch as attn_prefill.
+ * Where one applies, workspace_bytes below attn_prefill_workspace_size is
  * ATTN_ERR_WORKSPACE.  Its first 4096 bytes hold one flag word per pair of
- * query tiles: they must be zero before the workspace's first use, and
- * every call leaves them zero, so one workspace serves calls of any sizes
- * in turn (the rest of the workspace may hold anything).  Calls that share
+ * query tiles (balanced schedule) or the queue counter (first word): they
+ * must be zero before the workspace's first use, and every call leaves them
+ * zero, so one workspace serves calls of any sizes in turn (the rest of the
+ * workspace may hold anything).  The output is the same, bit for bit, with
+ * or without the tile queue: it changes only which workgroup computes a
+ * tile.  Calls that share
  * a workspace must not overlap in time (launch them on one stream).  A workgroup waits for its partner's part
  * for a bounded time only, then computes the part itself, so a launch
  * always completes.  Other arguments and errors as attn_prefill.
@@ -294,9 +318,9 @@ int attn_prefill_select(int kernel);
 
 /* The kernel (ATTN_PREFILL_W4, ATTN_PREFILL_RB or ATTN_PREFILL_KS) a dense
    16-bit prefill launch with these sizes would use under the current
-   setting, without a workspace (with one, the balanced schedule runs the RB
-   kernel, four heads per workgroup, wherever attn_prefill_workspace_size is
-   nonzero).  W4 launches B Hq ceil(S/128) workgroups of 256 threads; RB
+   setting, without a workspace (with one, the balanced schedule or the tile
+   queue runs the RB kernel, four heads per workgroup, wherever
+   attn_prefill_workspace_size is nonzero).  W4 launches B Hq ceil(S/128) workgroups of 256 threads; RB
    launches B (Hq/4) ceil(S/64) workgroups of 256 threads when Hq/Hkv is a
    multiple of 4, else B Hq ceil(S/128) of 128 threads; KS launches
    B Hq ceil(S/32) workgroups of 256 threads. */

@@ -34,7 +34,8 @@ def prefill_kernel(request):
     """Runs a prefill test under each 16-bit prefill kernel and schedule:
     the 4-wave kernel, the register-blocked one without a workspace, the
     register-blocked one with a workspace (the balanced causal schedule
-    where it applies, the register-blocked kernel elsewhere), and the
+    where it applies, the tile queue for causal launches of several rounds,
+    the register-blocked kernel's static order elsewhere), and the
     key-split kernel (dense calls without RoPE; the others take the 4-wave
     kernel).  The register-blocked kernel applies to head dim 128; at D = 64
     the rb runs use the 4-wave kernel.  Restores the automatic choice

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "attn_prefill_select", "attn_prefill_kernel_for",
               "attn_prefill_ws", "attn_prefill_ws_f16",
               "attn_prefill_workspace_size", "attn_prefill_split_wait",
-              "attn_prefill_residual_rmsnorm",
+              "attn_prefill_schedule", "attn_prefill_residual_rmsnorm",
               "attn_prefill_residual_rmsnorm_f16",
               "attn_status_string"]:
         assert n in names
@@ -116,7 +116,22 @@ def test_prefill_kernel_selection():
             assert attn.prefill_workgroups(1, 8, 2, 2048, 128) == (
                 KS, 8 * 64, 256)
             assert attn.prefill_balanced(1, 8, 2, 4096, 128)
+            # several rounds of register-blocked workgroups: the tile queue
+            Q = attn.SCHEDULE_QUEUE
+            assert attn.prefill_schedule(1, 8, 2, 32768, 128) == Q
+            assert not attn.prefill_balanced(1, 8, 2, 32768, 128)
+            assert attn.prefill_workgroups(1, 8, 2, 32768, 128) == (
+                RB, 2 * 512, 256)
+            assert attn.prefill_schedule(4, 8, 2, 2048, 128) == \
+                attn.SCHEDULE_BALANCED
+            assert attn.prefill_schedule(1, 8, 2, 32768, 128,
+                                         causal=False) == \
+                attn.SCHEDULE_STATIC
+            assert attn.lib().attn_prefill_schedule(1, 8, 3, 64, 128, 1) == \
+                attn.SCHEDULE_STATIC                  # invalid sizes
             attn.prefill_workspace_policy(False)
+            assert attn.prefill_schedule(1, 8, 2, 32768, 128) == \
+                attn.SCHEDULE_STATIC
             assert attn.prefill_workgroups(4, 8, 2, 2048, 128) == (
                 W4, 4 * 8 * 16, 256)
         finally:
@@ -200,18 +215,29 @@ def test_prefill_workspace_size():
         assert ws(4, 8, 2, 2048, 64) == 0          # head dim 64
         assert ws(4, 8, 4, 2048, 128) == 0         # group size 2
         assert ws(1, 8, 2, 64, 128) == 0           # one query tile
-        assert ws(8, 8, 2, 2048, 128) == 0         # two rounds of workgroups
+        assert ws(8, 8, 2, 2048, 128) == 0         # 4-wave kernel by the table
         assert ws(0, 8, 2, 2048, 128) == 0
+        # tile queue: register-blocked launches of several rounds (the first
+        # 4 KB only)
+        assert ws(1, 8, 2, 32768, 128) == 4096     # 1024 workgroups
+        assert ws(2, 8, 2, 8192, 128) == 4096      # 512
+        assert ws(1, 8, 2, 32768, 128, causal=False) == 0
+        assert ws(1, 12, 3, 32768, 128) == 4096    # 3 KV heads of 4 each
+        assert ws(1, 8, 4, 32768, 128) == 0        # group size 2
         # forced register-blocked kernel: wherever it applies; odd tile
         # count: the middle tile has no pair
         attn.prefill_select(attn.PREFILL_RB)
         assert ws(2, 8, 2, 300, 128) == 4096 + 2 * 2 * 2 * 4 * 33 * 64 * 16
         assert ws(1, 8, 2, 64, 128) == 0           # still one query tile
         assert ws(1, 8, 2, 2048, 128) == 4096 + 32 * 4 * 33 * 64 * 16
+        assert ws(8, 8, 2, 2048, 128) == 4096      # 512 workgroups: queue
+        assert ws(8, 8, 2, 2048, 128, causal=False) == 0
         attn.prefill_select(attn.PREFILL_W4)
         assert ws(4, 8, 2, 2048, 128) == 0
+        assert ws(1, 8, 2, 32768, 128) == 0
         attn.prefill_select(attn.PREFILL_KS)
         assert ws(4, 8, 2, 2048, 128) == 0
+        assert ws(1, 8, 2, 32768, 128) == 0
     finally:
         attn.prefill_select(prev)
 
