@@ -198,7 +198,7 @@ long long prefill_split_pairs(int B, int Hq, int Hkv, int S, int D,
 // queue: where that kernel is chosen, the balanced schedule is not, and the
 // launch holds more workgroups than compute units (in one round every
 // workgroup is resident from the start and the queue would only add its
-// atomic round trip).  The queue is the workspace's first word.
+// atomic round trip).  The queue counter is the workspace's first 8 bytes.
 bool prefill_queue_applies(int B, int Hq, int Hkv, int S, int D,
                            int causal) {
   if (!causal || D != 128 || B <= 0 || S <= 0 || Hkv <= 0 ||

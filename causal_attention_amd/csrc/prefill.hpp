@@ -104,16 +104,27 @@ struct TileCoord {
 // receives a fixed eighth of the blocks: measured on MI355X (B1, 8/2 heads,
 // S = 32768), the XCDs of one KV head ran their tiles 4% slower than the
 // others and finished up to 90 us after them, and the queue took the launch
-// from 1813-1822 to 1720 us.  The counter is zero between launches: the
-// workgroup that draws the launch's last index puts it back to zero (every
-// other workgroup of the launch has drawn by then), and an index is taken
-// modulo the block count, so each launch's draws are a permutation of its
-// blocks.
-__device__ __forceinline__ int queue_take(unsigned* ctr, unsigned nblocks) {
-  const unsigned v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-  if (v == nblocks - 1)
-    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// from 1813-1822 to 1720 us.
+//
+// The counter (64 bits) is zero between launches: the workgroup that draws
+// the launch's last index puts it back to zero, by a compare-and-swap that
+// succeeds only if nobody has drawn since (every other workgroup of the
+// launch has drawn by then).  An index is the draw modulo the block count.
+// Whatever the counter held at the start, each launch's draws are then a
+// permutation of its blocks: without a reset they are nblocks consecutive
+// values; with one, the values drawn before it run from the start value c
+// up to nblocks - 1 and those after it from 0 up to c - 1.  A nonzero start
+// only rotates the order.
+__device__ __forceinline__ int queue_take(unsigned long long* ctr,
+                                          unsigned nblocks) {
+  const unsigned long long v = __hip_atomic_fetch_add(
+      ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v == nblocks - 1ull) {
+    unsigned long long expected = nblocks;
+    __hip_atomic_compare_exchange_strong(ctr, &expected, 0ull,
+                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   return (int)(v % nblocks);
 }
 
@@ -978,7 +989,8 @@ void attn_prefill_rb_kernel(
     // tile queue: dense causal launches only (the host passes no workspace
     // to the other forms of this kernel)
     __shared__ int s_idx;
-    if (tid == 0) s_idx = queue_take(static_cast<unsigned*>(ws), gridDim.x);
+    if (tid == 0)
+      s_idx = queue_take(static_cast<unsigned long long*>(ws), gridDim.x);
     __syncthreads();
     tc = tile_coord(s_idx, gridDim.x, B, Hq / GQ, Hkv, n_qtiles, INT_MAX);
   } else {

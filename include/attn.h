@@ -123,12 +123,13 @@ int attn_prefill_schedule(int B, int Hq, int Hkv, int S, int D, int causal);
  * NULL, or a launch neither applies to: the same launch as attn_prefill.
  * Where one applies, workspace_bytes below attn_prefill_workspace_size is
  * ATTN_ERR_WORKSPACE.  Its first 4096 bytes hold one flag word per pair of
- * query tiles (balanced schedule) or the queue counter (first word): they
- * must be zero before the workspace's first use, and every call leaves them
- * zero, so one workspace serves calls of any sizes in turn (the rest of the
- * workspace may hold anything).  The output is the same, bit for bit, with
- * or without the tile queue: it changes only which workgroup computes a
- * tile.  Calls that share
+ * query tiles (balanced schedule) or the queue counter (first 8 bytes):
+ * they must be zero before the workspace's first use, and every call leaves
+ * them zero, so one workspace serves calls of any sizes in turn (the rest of
+ * the workspace may hold anything).  The output is the same, bit for bit,
+ * with or without the tile queue: it changes only which workgroup computes a
+ * tile (a nonzero counter still gives every tile to exactly one workgroup;
+ * it only changes their order).  Calls that share
  * a workspace must not overlap in time (launch them on one stream).  A workgroup waits for its partner's part
  * for a bounded time only, then computes the part itself, so a launch
  * always completes.  Other arguments and errors as attn_prefill.

@@ -184,3 +184,23 @@ def test_queue_graph_replay():
         say(f"   replay {t}: max|dO|={err:.3e}")
         assert err <= TOL["bf16"]
         assert np.abs(lse.cpu().numpy() - rl).max() <= LSE_TOL
+
+
+@pytest.mark.usefixtures("forced_rb")
+def test_queue_with_a_counter_left_nonzero():
+    """A workspace whose counter was not zeroed (5: below the block count,
+    so the reset happens mid-launch; 12345: above it, so it never does)
+    still gives every tile to exactly one workgroup: the output equals the
+    static order's bit for bit, on two calls in a row."""
+    B, Hq, Hkv, S = 9, 8, 2, 1000          # 288 workgroups
+    q, k, v = load(B, Hq, Hkv, S, "bf16", 40)
+    so, sl = static_run(q, k, v)
+    for start in (5, 12345):
+        ws = attn.new_prefill_workspace(B, Hq, Hkv, S, 128, device=DEV)
+        ws[:8].copy_(torch.tensor([start], dtype=torch.int64).view(
+            torch.uint8).to(DEV))
+        for rep in range(2):
+            say(f"[queue nonzero counter] start={start} rep={rep}")
+            o, lse = attn.attn_prefill(q, k, v, causal=True, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o, so) and torch.equal(lse, sl)
