@@ -204,3 +204,36 @@ def test_queue_with_a_counter_left_nonzero():
             o, lse = attn.attn_prefill(q, k, v, causal=True, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(o, so) and torch.equal(lse, sl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_queue_long_context_sampled(dtype):
+    """The long-context shape (B1, 8/2 heads, S = 32768, 1024 workgroups)
+    under the automatic choice, which runs the tile queue: sampled rows
+    against the oracle, every row finite, and the whole output equal to the
+    static order's."""
+    B, Hq, Hkv, S = 1, 8, 2, 32768
+    prev = attn.prefill_select(attn.PREFILL_AUTO)
+    prev_ws = attn.prefill_workspace_policy(True)
+    try:
+        say(f"[queue long] B={B} Hq={Hq} Hkv={Hkv} S={S} {dtype}")
+        assert attn.prefill_schedule(B, Hq, Hkv, S, 128) == \
+            attn.SCHEDULE_QUEUE
+        q, k, v = load(B, Hq, Hkv, S, dtype, 11)
+        o, lse = attn.attn_prefill(q, k, v, causal=True)
+        so, sl = static_run(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, so) and torch.equal(lse, sl)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        rows = inputs.sampled_rows(Hq, S, 32)
+        ro, rl = oracle.prefill_rows(np64(q), np64(k), np64(v),
+                                     1 / math.sqrt(128), True, rows)
+        oc, lc = o.cpu(), lse.cpu()
+        go = np.stack([np64(oc[:, h, rows[h]]) for h in range(Hq)], axis=1)
+        gl = np.stack([lc[:, h, rows[h]].numpy() for h in range(Hq)], axis=1)
+        eo, el = np.abs(go - ro).max(), np.abs(gl - rl).max()
+        say(f"   sampled rows: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= TOL[dtype] and el <= LSE_TOL
+    finally:
+        attn.prefill_select(prev)
+        attn.prefill_workspace_policy(prev_ws)
